@@ -1,0 +1,389 @@
+"""Pins of the CPU oracle to facts fixed outside itself: format definitions,
+hand-derived fixtures, closed forms, invariants and brute force computed by a
+different route (Python integers, exact rationals, dequantize-then-matmul).
+
+A plausible slip in the oracle (dropped term, wrong sign or index,
+transposed operand, wrong rounding) fails at least one of these.
+"""
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32(v) -> float:
+    """Round a Python float (binary64) to binary32."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def _rne_int(fr: Fraction) -> int:
+    """Round an exact rational to the nearest integer, ties to even."""
+    fl = fr.numerator // fr.denominator
+    rem = fr - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        return fl + 1
+    return fl
+
+
+# ---------------------------------------------------------------- int8 act quant
+
+def test_int8_ties_fixture():
+    lines = [l for l in open(os.path.join(GOLD, "int8_act_ties.txt")) if not l.startswith("#")]
+    vals = {l.split(":")[0]: l.split(":")[1].split() for l in lines if ":" in l}
+    x = np.array([float(v) for v in vals["x"]], dtype=np.float32)[None, :]
+    codes, s = O.quantize_act_int8(x)
+    assert s[0] == np.float32(vals["scale"][0])
+    assert codes[0].tolist() == [int(c) for c in vals["codes"]]
+
+
+def test_int8_bruteforce_all_bf16_patterns():
+    """Every finite bf16 value, placed in rows of fixed absmax, against exact
+    rational arithmetic: scale = f32(amax/127); code = rne(f32(x/scale))."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = O.bf16_bits_to_f32(bits)
+    v = v[np.isfinite(v)]
+    for amax in (1.0, 3.0, 448.0, 1e-3, 7.25):
+        row = v[np.abs(v) <= amax]
+        x = np.concatenate([[np.float32(amax)], row]).astype(np.float32)[None, :]
+        codes, s = O.quantize_act_int8(x)
+        s_ref = _f32(amax / 127.0)               # binary64 divide then round: correctly rounded
+        assert float(s[0]) == s_ref
+        # f64 quotient rounded to f32 is the correctly rounded f32 quotient (53 >= 2*24+2)
+        q32 = np.array([_f32(float(t) / s_ref) for t in x[0]], dtype=np.float64)
+        ref = np.array([max(-127, min(127, _rne_int(Fraction(q)))) for q in q32])
+        assert np.array_equal(codes[0].astype(np.int64), ref)
+
+
+def test_int8_invariants_random_rows():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((64, 300)) * rng.uniform(1e-3, 1e3, (64, 1))).astype(np.float32)
+    x[5] = 0.0
+    codes, s = O.quantize_act_int8(x)
+    assert s[5] == 0 and not codes[5].any()
+    nz = np.arange(64) != 5
+    assert np.all(np.abs(codes[nz]).max(axis=1) == 127)          # absmax maps to 127
+    assert np.all((np.sign(codes) == np.sign(x)) | (codes == 0))  # sign kept or zero
+    assert codes.min() >= -127                                     # -128 never produced
+    err = np.abs(x[nz].astype(np.float64) / s[nz, None].astype(np.float64) - codes[nz])
+    assert err.max() <= 0.5 + 1e-5
+
+
+# ---------------------------------------------------------------- fp8 e4m3
+
+def _e4m3_value_exact(code: int) -> Fraction:
+    s = -1 if code & 0x80 else 1
+    e = (code >> 3) & 0xF
+    m = code & 7
+    if e == 0:
+        return s * Fraction(m, 2 ** 9)
+    return s * Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+
+
+def test_e4m3_fixture():
+    for line in open(os.path.join(GOLD, "e4m3_codes.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        v, c = line.split()
+        got = int(O.e4m3_encode(np.array([float(v)], dtype=np.float32))[0])
+        assert got == int(c, 16), (v, hex(got), c)
+
+
+def test_e4m3_decode_matches_exact_definition():
+    for c in range(256):
+        d = O.e4m3_decode(np.array([c], dtype=np.uint8))[0]
+        if c & 0x7F == 0x7F:
+            assert np.isnan(d)
+        else:
+            assert Fraction(d) == _e4m3_value_exact(c)
+
+
+def test_e4m3_roundtrip_all_codes():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = O.e4m3_decode(codes).astype(np.float32)
+    assert np.array_equal(O.e4m3_encode(vals), codes)
+
+
+def test_e4m3_encode_is_nearest_even_bruteforce():
+    """Against a scan over all finite codes with exact rationals."""
+    finite = [c for c in range(128) if c != 0x7F]
+    exact = {c: _e4m3_value_exact(c) for c in finite}
+    rng = np.random.default_rng(3)
+    # random magnitudes across the whole range, plus every midpoint and its neighbours
+    mags = list(np.exp2(rng.uniform(-12, 9.2, 3000)).astype(np.float32))
+    srt = sorted(finite, key=lambda c: exact[c])
+    for a, b in zip(srt[:-1], srt[1:]):
+        mid = np.float32(float((exact[a] + exact[b]) / 2))
+        mags += [mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e9))]
+    v = np.array(mags, dtype=np.float32)
+    v = np.concatenate([v, -v])
+    got = O.e4m3_encode(v)
+    for x, c in zip(v, got):
+        a = Fraction(float(abs(x)))
+        a = min(a, Fraction(448))
+        best = min(finite, key=lambda k: (abs(exact[k] - a), k % 2))
+        want = best | (0x80 if np.signbit(x) else 0)
+        assert int(c) == want, (float(x), hex(int(c)), hex(want))
+
+
+def test_fp8_act_quant_rows():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((32, 200)).astype(np.float32)
+    x[3] = 0
+    codes, s = O.quantize_act_fp8(x)
+    assert s[3] == 0 and not codes[3].any()
+    dec = O.e4m3_decode(codes)
+    nz = np.arange(32) != 3
+    assert np.all(np.abs(dec[nz]).max(axis=1) == 448.0)           # absmax row hits 448
+    assert np.all(s[nz] == (np.abs(x[nz]).max(axis=1) / np.float32(448)).astype(np.float32))
+    # relative error of each code within half an E4M3 ulp (2^-4) in the normal range
+    xs = x[nz].astype(np.float64) / s[nz, None]
+    big = np.abs(xs) >= 2.0 ** -6
+    assert np.all(np.abs(dec[nz][big] - xs[big]) <= np.abs(xs[big]) * 2.0 ** -4 + 1e-12)
+
+
+def test_int4_values_exact_in_e4m3():
+    v = np.arange(-8, 8, dtype=np.float32)
+    assert np.array_equal(O.e4m3_decode(O.e4m3_encode(v)), v.astype(np.float64))
+
+
+# ---------------------------------------------------------------- layouts
+
+def test_gptq_word_fixture():
+    for line in open(os.path.join(GOLD, "gptq_words.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        parts = line.split()
+        w = np.array([[int(parts[0], 16)]], dtype=np.uint32).view(np.int32)
+        assert O.unpack_gptq_kn(w)[:, 0].tolist() == [int(p) for p in parts[1:]]
+        assert O.unpack_ct_nk(w)[0].tolist() == [int(p) for p in parts[1:]]
+
+
+def test_gptq_unpack_bruteforce_python_ints():
+    rng = np.random.default_rng(5)
+    qw = rng.integers(0, 2 ** 32, (6, 5), dtype=np.uint32).view(np.int32)
+    q = O.unpack_gptq_kn(qw)
+    assert q.shape == (48, 5)
+    for k in range(48):
+        for n in range(5):
+            word = int(qw.view(np.uint32)[k // 8, n])
+            assert q[k, n] == (word // 16 ** (k % 8)) % 16
+
+
+def test_pack_unpack_roundtrip_and_extremes():
+    rng = np.random.default_rng(9)
+    for q in (rng.integers(0, 16, (7, 64)), np.zeros((3, 8), int), np.full((3, 8), 15)):
+        q = q.astype(np.uint8)
+        assert np.array_equal(O.unpack_nibble_bytes(O.pack_nibble_bytes(q)), q)
+    b = rng.integers(0, 256, (4, 16), dtype=np.uint8)
+    assert np.array_equal(O.pack_nibble_bytes(O.unpack_nibble_bytes(b)), b)
+
+
+def test_int32_words_are_the_byte_stream():
+    """8 codes per little-endian int32 == two codes per byte (zentorch page)."""
+    rng = np.random.default_rng(1)
+    w = rng.integers(0, 2 ** 32, (9, 12), dtype=np.uint32).view(np.int32)
+    assert np.array_equal(O.unpack_ct_nk(w), O.unpack_nibble_bytes(w.view(np.uint8)))
+
+
+def test_xor_0x88_exhaustive():
+    """Signed int4 (two's complement nibble) s -> uint4b8 code s + 8, per nibble."""
+    for lo in range(-8, 8):
+        for hi in range(-8, 8):
+            byte = (lo & 0xF) | ((hi & 0xF) << 4)
+            word = np.array([byte, 0x00, 0x00, 0x00], dtype=np.uint8)   # other nibbles: 0 -> 8
+            out = O.repack_signed_int4_to_uint4b8(word)
+            codes = O.unpack_ct_nk(out.reshape(1, 1))[0]
+            assert codes[0] == lo + 8 and codes[1] == hi + 8
+            assert np.all(codes[2:] == 8)
+
+
+# ---------------------------------------------------------------- partials / epilogue
+
+def test_partials_bruteforce_python_ints():
+    rng = np.random.default_rng(21)
+    M, K, N, g = 3, 64, 5, 32
+    codes = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    qw = rng.integers(0, 2 ** 32, (K // 8, N), dtype=np.uint32).view(np.int32)
+    P = O.group_partials(codes, O.unpack_gptq_kn(qw), g)
+    for m in range(M):
+        for gg in range(K // g):
+            for n in range(N):
+                s = 0
+                for k in range(gg * g, (gg + 1) * g):
+                    word = int(qw.view(np.uint32)[k // 8, n])
+                    s += int(codes[m, k]) * (((word >> (4 * (k % 8))) & 15) - 8)
+                assert P[m, gg, n] == s
+
+
+def test_partials_additive_and_group_minus1_is_K():
+    rng = np.random.default_rng(22)
+    M, K, N = 9, 512, 24
+    codes = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    P128 = O.group_partials(codes, q, 128)
+    Pch = O.group_partials(codes, q, -1)
+    PK = O.group_partials(codes, q, K)
+    assert Pch.shape == (M, 1, N)
+    assert np.array_equal(P128.sum(axis=1), Pch[:, 0])
+    assert np.array_equal(Pch, PK)
+    assert np.abs(Pch).max() <= 127 * 8 * K
+
+
+def test_epilogue_vs_dequantize_then_matmul():
+    rng = np.random.default_rng(23)
+    M, K, N, g = 6, 256, 40, 64
+    codes = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    s_a = rng.uniform(0.001, 0.1, M).astype(np.float32)
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    sc = rng.uniform(0.005, 0.02, (K // g, N)).astype(np.float16)
+    bias = rng.standard_normal(N)
+    y = O.w4a8_epilogue(O.group_partials(codes, q, g), s_a, sc.astype(np.float32), bias)
+    Xh = codes.astype(np.float64) * s_a.astype(np.float64)[:, None]
+    Wh = (q.astype(np.float64) - 8.0) * np.repeat(sc.astype(np.float64), g, axis=0)
+    ref = Xh @ Wh + bias
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_epilogue_one_hot_and_all_eights():
+    rng = np.random.default_rng(24)
+    K, N, g = 256, 16, 128
+    qw = rng.integers(0, 2 ** 32, (K // 8, N), dtype=np.uint32).view(np.int32)
+    sc = rng.uniform(0.005, 0.02, (K // g, N)).astype(np.float16)
+    k0, alpha = 170, 3.25
+    x = np.zeros((1, K), np.float32)
+    x[0, k0] = alpha
+    xb = x.view(np.uint32) >> 16                      # exact bf16 bits (alpha is exact)
+    out = O.w4a8_reference(xb.astype(np.uint16), "bf16", qw, sc, g)
+    q = O.unpack_gptq_kn(qw)
+    want = alpha * (q[k0].astype(np.float64) - 8) * sc[k0 // g].astype(np.float64)
+    assert np.allclose(out["y"][0], want, rtol=1e-6)
+    # all codes 8 => zero weights => y == bias
+    qw8 = np.full((K // 8, N), 0x88888888, dtype=np.uint32).view(np.int32)
+    xb2 = (rng.standard_normal((4, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bias = (rng.standard_normal(N).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out8 = O.w4a8_reference(xb2, "bf16", qw8, sc, g, bias_bits=bias)
+    assert np.array_equal(out8["y"], np.broadcast_to(O.bf16_bits_to_f32(bias).astype(np.float64), (4, N)))
+
+
+def test_equal_scales_grouped_equals_per_channel():
+    rng = np.random.default_rng(25)
+    M, K, N = 5, 384, 32
+    codes = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    s_a = rng.uniform(0.01, 0.1, M).astype(np.float32)
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    col = rng.uniform(0.005, 0.02, N).astype(np.float16).astype(np.float32)
+    y_g = O.w4a8_epilogue(O.group_partials(codes, q, 128), s_a, np.tile(col, (K // 128, 1)))
+    y_c = O.w4a8_epilogue(O.group_partials(codes, q, -1), s_a, col[None, :])
+    assert np.allclose(y_g, y_c, rtol=1e-13, atol=0)
+
+
+# ---------------------------------------------------------------- W4A16
+
+def test_w4a16_factored_identity_and_one_hot():
+    rng = np.random.default_rng(31)
+    M, K, N, g = 3, 256, 20, 64
+    xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    wb = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sb = (rng.uniform(0.005, 0.02, (N, K // g)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    zb = ((rng.standard_normal((N, K // g)) * 0.01).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = O.w4a16_reference(xb, wb, sb, zb, g)
+    # factored form by loops: y = sum_g s*sum x(q-8) + z*sum x
+    x = O.bf16_bits_to_f32(xb).astype(np.float64)
+    s = O.bf16_bits_to_f32(sb).astype(np.float64)
+    z = O.bf16_bits_to_f32(zb).astype(np.float64)
+    ref = np.zeros((M, N))
+    for n in range(N):
+        row = wb[n]
+        codes = [(int(row[j // 2]) >> (4 * (j % 2))) & 15 for j in range(K)]
+        for m in range(M):
+            tot = 0.0
+            for gg in range(K // g):
+                ks = range(gg * g, (gg + 1) * g)
+                tot += s[n, gg] * sum(x[m, k] * (codes[k] - 8) for k in ks) + z[n, gg] * sum(x[m, k] for k in ks)
+            ref[m, n] = tot
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # one-hot x picks one dequantized weight column
+    k0 = 77
+    xo = np.zeros((1, K), np.uint16)
+    xo[0, k0] = 0x3F80                                      # bf16 1.0
+    y1 = O.w4a16_reference(xo, wb, sb, zb, g)[0]
+    q = O.unpack_nibble_bytes(wb)[:, k0].astype(np.float64)
+    assert np.array_equal(y1, (q - 8) * s[:, k0 // g] + z[:, k0 // g])
+
+
+def test_quantize_groupwise_reproduces_extremes():
+    rng = np.random.default_rng(32)
+    w = rng.standard_normal((12, 128)) * 0.05
+    q, s, z = O.quantize_groupwise(w, 64)
+    deq = O.dequantize_groupwise(q, s, z, 64)
+    wf = w.reshape(12, 2, 64)
+    lo = (0.0 - 8) * s + z
+    hi = (15.0 - 8) * s + z
+    assert np.allclose(lo, wf.min(-1), rtol=0, atol=1e-12)
+    assert np.allclose(hi, wf.max(-1), rtol=0, atol=1e-12)
+    assert np.all(np.abs(deq - w) <= np.repeat(s, 64, axis=1) / 2 + 1e-12)
+    assert q.min() == 0 and q.max() == 15
+    with pytest.raises(ValueError):
+        O.quantize_groupwise(w[:, :100], 64)
+
+
+# ---------------------------------------------------------------- routed experts
+
+def _tiny_moe(seed=41, E=4, K=256, N=64, T=32, topk=2):
+    from int4_weight_quantized_amd import workloads as W
+    return W.moe_inputs(E, K, N, 128, T, topk, seed)
+
+
+def test_routing_structure():
+    d = _tiny_moe()
+    rt, off = d["row_token"], d["expert_offsets"]
+    assert off[0] == 0 and off[-1] == d["T"] * d["topk"] and np.all(np.diff(off) >= 0)
+    pairs = set()
+    for e in range(d["E"]):
+        toks = rt[off[e]:off[e + 1]]
+        assert np.all(np.diff(toks) > 0)                    # stable by token, no duplicates
+        pairs |= {(int(t), e) for t in toks}
+    per_tok = np.bincount([t for t, _ in pairs], minlength=d["T"])
+    assert np.all(per_tok == d["topk"])
+
+
+def test_grouped_bruteforce_and_segments():
+    d = _tiny_moe()
+    x32 = O.bf16_bits_to_f32(d["x"])
+    a8, s_a = O.quantize_act_fp8(x32)
+    y = O.grouped_fp8_reference(a8, s_a, d["row_token"], d["expert_offsets"], d["w"], d["scales"], 128)
+    off = d["expert_offsets"]
+    # brute force: dequantize activations and weights fully, per routed row
+    for e in range(d["E"]):
+        Wd = np.zeros((d["K"], d["N"]))
+        for n in range(d["N"]):
+            for k in range(d["K"]):
+                word = int(d["w"].view(np.uint32)[e, n, k // 8])
+                qv = (word >> (4 * (k % 8))) & 15
+                Wd[k, n] = (qv - 8) * float(d["scales"][e, k // 128, n])
+        for r in range(off[e], off[e + 1]):
+            t = d["row_token"][r]
+            xa = O.e4m3_decode(a8[t]) * float(s_a[t])
+            assert np.allclose(y[r], xa @ Wd, rtol=1e-12, atol=1e-12)
+    # a row subset gives the same numbers
+    rows = np.array([5, 0, 63, 17])
+    ys = O.grouped_fp8_reference(a8, s_a, d["row_token"], off, d["w"], d["scales"], 128, rows=rows)
+    assert np.array_equal(ys, y[rows])
+
+
+def test_grouped_single_expert_is_dense():
+    d = _tiny_moe(seed=42, E=1, T=16, topk=1)
+    x32 = O.bf16_bits_to_f32(d["x"])
+    a8, s_a = O.quantize_act_fp8(x32)
+    y = O.grouped_fp8_reference(a8, s_a, d["row_token"], d["expert_offsets"], d["w"], d["scales"], 128)
+    assert np.array_equal(d["row_token"], np.arange(16))
+    A = O.e4m3_decode(a8) * s_a.astype(np.float64)[:, None]
+    q = O.unpack_ct_nk(d["w"][0]).astype(np.float64) - 8
+    Wd = q * np.repeat(d["scales"][0].astype(np.float64), 128, axis=0).T
+    assert np.allclose(y, A @ Wd.T, rtol=1e-12, atol=1e-12)
