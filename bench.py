@@ -1,0 +1,244 @@
+"""Benchmark of the int4-weight quantized linear layer on one MI355X.
+
+Timed step: one W4A8 forward of the MLP up-projection workload (M=4096
+tokens, K=4096, N=14336, group 128, bf16 activations): per-token int8
+quantization followed by the W4A8 GEMM with its fused epilogue, inputs
+resident in HBM. `value` is 2*M*N*K / step time in TOPS.
+
+Measured in the same run and reported beside it:
+  decode  W4A16 decode (M=1 and M=8, K=4096, N=14336, group 64), achieved
+          HBM GB/s with weights rotated through 16 distinct sets (> MALL)
+  moe     W4A-FP8 routed experts (64 experts, K=7168, N=2048, 8192 tokens,
+          top-8): FP8 quantization + grouped GEMM
+  roofline  the dominant kernel (the W4A8 GEMM) against the int8 MFMA peak,
+          its duration from HIP events on the launch stream
+  cpu_baseline  the CPU oracle timed on a bounded row sample of the step
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP8_TFLOPS = 5000.0    # dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # HBM3E 8 TB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--only", choices=["all", "w4a8", "decode", "moe"], default="all")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    return p.parse_args()
+
+
+def src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "int4_weight_quantized_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key: str, srcs, n_launch_units: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if absent or taken on a different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != src_hash(*srcs):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int4_weight_quantized_amd import ops, workloads as W
+
+    if not os.path.exists(ops.LIB_PATH):
+        from int4_weight_quantized_amd import build as B
+        B.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def dev_half(bits, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(dev)
+
+    def timed(fns, steps, warmup):
+        """Run the list of launch callables per step; return mean ms per callable
+        (HIP events on the launch stream) and the mean step time."""
+        for _ in range(warmup):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for s in range(steps):
+            ev[s][0].record(stream)
+            for i, f in enumerate(fns):
+                f()
+                ev[s][i + 1].record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+               for i in range(len(fns))]
+        return per, start.elapsed_time(end) / steps, wall
+
+    # ------------------------------------------------------------ W4A8 up-proj step
+    d = W.named("w4a8_up_proj")
+    M, K, N, g = d["M"], d["K"], d["N"], d["group"]
+    x = dev_half(d["x"], "bf16")
+    qw = torch.from_numpy(d["qweight"]).to(dev)
+    sc = torch.from_numpy(d["scales"]).to(dev)
+    wt = ops.w4_repack(qw, ops.W4_LAYOUT_GPTQ_KN, K, N)
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s_a = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fq = lambda: ops.quantize_act_into(x, codes, s_a)
+    fg = lambda: ops.w4a8_gemm(codes, s_a, wt, sc, g, N, out=y)
+    (t_q, t_g), t_step, _ = timed([fq, fg], args.steps, args.warmup)
+    ops_gemm = 2.0 * M * N * K
+    tops = ops_gemm / (t_step * 1e-3) / 1e12
+    tops_gemm = ops_gemm / (t_g * 1e-3) / 1e12
+    quant_bytes = M * K * 2 + M * K + M * 4
+    w4a8 = {
+        "workload": f"w4a8_up_proj M={M} K={K} N={N} group={g} bf16",
+        "quant_ms": t_q, "gemm_ms": t_g, "step_ms": t_step,
+        "gemm_tops": tops_gemm, "gemm_frac_int8_peak": tops_gemm / PEAK_INT8_TOPS,
+        "quant_gbs": quant_bytes / (t_q * 1e-3) / 1e9,
+    }
+
+    # ------------------------------------------------------------ W4A16 decode
+    decode = {}
+    if args.only in ("all", "decode"):
+        nrot = 16
+        for Md in (1, 8):
+            dd = W.named("w4a16_decode", M=Md)
+            Kd, Nd, gd = dd["K"], dd["N"], dd["group"]
+            xd = dev_half(dd["x"], "bf16")
+            base_w = torch.from_numpy(dd["w"]).to(dev)
+            base_s = dev_half(dd["scale"], "bf16")
+            base_z = dev_half(dd["zero"], "bf16")
+            sets = [(base_w.roll(i, 0).contiguous(), base_s.roll(i, 0).contiguous(),
+                     base_z.roll(i, 0).contiguous()) for i in range(nrot)]
+            yd = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
+            calls = [(lambda st=st: ops.w4a16_gemm(xd, st[0], st[1], st[2], gd, out=yd)) for st in sets]
+            reps = max(1, args.steps // 4)
+            per, _, _ = timed(calls, reps, max(1, args.warmup // 4))
+            t = float(np.mean(per))
+            nbytes = Nd * Kd // 2 + 2 * 2 * Nd * (Kd // gd) + 2 * Md * Kd + 2 * Md * Nd
+            decode[f"M{Md}"] = {"us": t * 1e3, "bytes": nbytes, "gbs": nbytes / (t * 1e-3) / 1e9,
+                                "frac_hbm": nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            del sets
+
+    # ------------------------------------------------------------ MoE grouped
+    moe = {}
+    if args.only in ("all", "moe"):
+        dm = W.named("w4afp8_moe")
+        Em, Km, Nm, gm, Tm = dm["E"], dm["K"], dm["N"], dm["group"], dm["T"]
+        xm = dev_half(dm["x"], "bf16")
+        wm = ops.w4_repack(torch.from_numpy(dm["w"]).to(dev), ops.W4_LAYOUT_CT_NK, Km, Nm, batch=Em)
+        scm = torch.from_numpy(dm["scales"]).to(dev)
+        rt = torch.from_numpy(dm["row_token"]).to(dev)
+        off = torch.from_numpy(dm["expert_offsets"]).to(dev)
+        R = rt.shape[0]
+        a8 = torch.empty((Tm, Km), dtype=torch.uint8, device=dev)
+        sm = torch.empty((Tm,), dtype=torch.float32, device=dev)
+        gs = torch.empty((Tm, Km // gm), dtype=torch.float32, device=dev)
+        ym = torch.empty((R, Nm), dtype=torch.bfloat16, device=dev)
+        fq8 = lambda: ops.quantize_act_into(xm, a8, sm, gs, gm, fp8=True)
+        fgg = lambda: ops.w4a8_grouped_gemm(a8, sm, gs, rt, off, wm, scm, gm, Nm, out=ym)
+        (t_q8, t_gg), t_moe, _ = timed([fq8, fgg], max(2, args.steps // 4), max(1, args.warmup // 2))
+        flops = 2.0 * R * Nm * Km
+        moe = {"workload": f"w4afp8_moe E={Em} K={Km} N={Nm} group={gm} T={Tm} top{dm['topk']} R={R}",
+               "quant_ms": t_q8, "grouped_gemm_ms": t_gg, "step_ms": t_moe,
+               "gemm_tflops": flops / (t_gg * 1e-3) / 1e12,
+               "gemm_frac_fp8_peak": flops / (t_gg * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        del wm
+
+    # ------------------------------------------------------------ roofline of the dominant kernel
+    achieved = ops_gemm / (t_g * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_INT8_TOPS,
+                "traffic": traffic_from_profile("w4a8_gemm_up_proj", ["w4a8_gemm.hip", "w4_device.h"], 1),
+                "kernel": "w4a8_gemm_kernel (int8 ops counted as TOPS)"}
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(d, args.cpu_seconds)
+
+    line = {
+        "metric": "W4A8 GEMM TOPS & % int8 MFMA peak (M=4096); W4A16 decode GB/s & % HBM",
+        "value": tops, "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": w4a8["workload"], "global_batch": M, "seq_len": 1, "parallelism": "single_gpu",
+                   "step": "w4a8_quantize_act + w4a8_gemm"},
+        "w4a8": w4a8, "decode": decode, "moe": moe,
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(d, target_s: float):
+    """The oracle as it stands on a row sample of the same layer: per-token
+    quantization of the sampled rows, exact int32 group partials and the
+    epilogue. Reported in the same unit (TOPS over the sampled rows)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    K, N, g = d["K"], d["N"], d["group"]
+    q = O.unpack_gptq_kn(d["qweight"])
+    sc = d["scales"].astype(np.float32)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        x32 = O.half_bits_to_f32(d["x"][:rows], d["x_dtype"])
+        codes, s = O.quantize_act_int8(x32)
+        P = O.group_partials(codes, q, g)
+        O.w4a8_epilogue(P, s, sc)
+        return time.perf_counter() - t0
+
+    t_small = run(16)
+    rows = int(min(d["M"], max(16, 16 * target_s / max(t_small, 1e-3))))
+    t = run(rows)
+    return {"value": 2.0 * rows * N * K / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {d['M']} rows of w4a8_up_proj (quantize + group partials + epilogue), "
+                      f"{t:.1f} s", "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

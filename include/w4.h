@@ -1,0 +1,217 @@
+/*
+ * w4.h -- C ABI of the int4-weight quantized linear layer for AMD Instinct
+ * MI355X (gfx950). Shared library: libw4.so.
+ *
+ * Sources (cited by page title and symbol):
+ *   [inc_w4a8]  vLLM docs page vllm.model_executor.layers.quantization.inc.
+ *               schemes.inc_w4a8_linear, class INCXPUW4A8LinearMethod
+ *   [ct_w4a8]   vLLM v0.10.1.1 docs page vllm.model_executor.layers.
+ *               quantization.compressed_tensors.schemes.compressed_tensors_w4a8_int
+ *   [w4afp8]    vLLM docs page vllm.model_executor.layers.quantization.w4afp8
+ *   [zentorch]  vLLM docs page vllm.model_executor.kernels.linear.
+ *               mixed_precision.zentorch, class ZentorchWNA16LinearKernel
+ *   [cpu_int4]  vllm-omni page model_executor/layers/quantization/cpu_int4.py
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers; the caller allocates
+ *     and owns every buffer. The library allocates nothing and keeps no state
+ *     but the per-thread error message.
+ *   - `stream` is a hipStream_t (NULL: the default stream). Work is enqueued
+ *     on it; no entry point synchronizes.
+ *   - Arguments are validated before anything is enqueued. On failure the
+ *     return value is a negative W4_ERR_* code and w4_last_error() names the
+ *     offending argument and sizes; nothing was launched.
+ *   - Sizes are element counts; matrices are row-major.
+ *   - A weight code q in 0..15 stands for the integer q - 8 ("uint4b8": the
+ *     zero point is the constant 8) [w4afp8] _repack_signed_int4_to_uint4b8;
+ *     within a packed word the code with the lowest K index is in the lowest
+ *     nibble ([cpu_int4] pack_nibbles; [zentorch] int32 words are the same
+ *     little-endian byte stream as two codes per byte).
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define W4_OK               0
+#define W4_ERR_INVALID     -1  /* null pointer, negative or zero size, bad enum value */
+#define W4_ERR_ALIGN       -2  /* K or N not a multiple of 8 ([inc_w4a8] create_weights
+                                  requires both GEMM dims to be multiples of 8), or a
+                                  pointer / leading dimension not 16-byte aligned */
+#define W4_ERR_GROUP       -3  /* group size not accepted (see each entry point) */
+#define W4_ERR_DTYPE       -4  /* element type not accepted */
+#define W4_ERR_UNSUPPORTED -5  /* shape outside what the kernels handle */
+#define W4_ERR_HIP         -6  /* a HIP launch reported an error */
+
+/* Element types. */
+#define W4_BF16      1
+#define W4_F16       2
+#define W4_F32       3
+#define W4_I8        4
+#define W4_FP8_E4M3  5   /* OCP E4M3FN: bias 7, max 448, no infinities */
+
+/* Source layouts of packed int4 weights accepted by w4_repack. */
+#define W4_LAYOUT_GPTQ_KN  1  /* int32 [K/8, N]: 8 codes per word along K; the output
+                                 dim is the second ([inc_w4a8] qweight, "NT" layout) */
+#define W4_LAYOUT_CT_NK    2  /* int32 [N, K/8]: compressed-tensors weight_packed,
+                                 packed along the input dim ([zentorch]) */
+#define W4_LAYOUT_S4_NK    3  /* int8 [N, K/2]: signed int4 two per byte (two's
+                                 complement nibbles, value = nibble); converted with
+                                 XOR 0x88 ([w4afp8] _repack_signed_int4_to_uint4b8) */
+
+/*
+ * Per-token dynamic activation quantization.
+ * [inc_w4a8] docstring and apply_weights: activations are quantized per token
+ * to symmetric int8 at run time (scale = absmax / 127). [w4afp8]
+ * W4AFP8Config: routed-expert activations are quantized per token to 8-bit
+ * float, symmetric and dynamic (scale = absmax / 448).
+ *
+ * For each row m:  a = max_k |x[m,k]| (fp32);  s = a / c  (fp32, correctly
+ * rounded; c = 127 for W4_I8, 448 for W4_FP8_E4M3);
+ *   W4_I8:       code = clamp(rne(x / s), -127, 127)       (fp32 divide)
+ *   W4_FP8_E4M3: code = E4M3(x / s), nearest-even, saturating at +-448
+ * An all-zero row gives s = 0 and codes 0. Non-finite inputs: unspecified.
+ *
+ *   x         device, [M, K] with row stride ldx elements; bf16 or fp16
+ *   x_dtype   W4_BF16 or W4_F16
+ *   ldx       >= K, a multiple of 8; x must be 16-byte aligned
+ *   codes     device, [M, K] contiguous, int8 or E4M3 bytes
+ *   code_dtype W4_I8 or W4_FP8_E4M3
+ *   scales    device, [M] fp32
+ *   group_sums device or NULL, [M, K/group] fp32 (FP8 only): the sum over
+ *             each K-group of the decoded FP8 code values of the row, in
+ *             fp32. w4a8_grouped_gemm needs it to apply the zero point 8.
+ *   group     group size for group_sums (> 0, divides K, multiple of 8);
+ *             ignored when group_sums is NULL
+ * Errors: INVALID (null, M/K < 0), ALIGN (K % 8, ldx, alignment),
+ *         DTYPE, GROUP, HIP.
+ */
+int w4a8_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                      void* codes, int code_dtype, float* scales,
+                      float* group_sums, int64_t group, void* stream);
+
+/*
+ * Size in bytes of one weight matrix in the kernel-tiled layout produced by
+ * w4_repack (tiles of 128 output columns x 128 K, 8 KiB each, ragged edges
+ * padded with code 8, i.e. zero weight).
+ *   bytes  host pointer receiving the size
+ * Errors: INVALID, ALIGN (K or N % 8).
+ */
+int w4_repack_bytes(int64_t K, int64_t N, size_t* bytes);
+
+/*
+ * Load-time repack of `batch` int4 weight matrices [K x N] (batch = number
+ * of experts; 1 for a dense layer) from a source layout into the kernel-tiled
+ * layout read by w4a8_gemm and w4a8_grouped_gemm. Codes are unchanged
+ * (apart from the XOR 0x88 that turns signed int4 into uint4b8 codes for
+ * W4_LAYOUT_S4_NK). [inc_w4a8] GPTQ qweight; [zentorch] compressed-tensors
+ * weight_packed; [w4afp8] signed-int4 checkpoints.
+ *   src     device, batch matrices back to back in `layout`
+ *   dst     device, batch * w4_repack_bytes(K, N) bytes, 16-byte aligned
+ * Errors: INVALID, ALIGN, HIP.
+ */
+int w4_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch,
+              void* dst, void* stream);
+
+/*
+ * W4A8 GEMM with fused dequantization epilogue.
+ * [inc_w4a8] apply_weights: int8 activation codes with per-token scales times
+ * int4 weights with fp16 scales per K-group (or per output column), bias
+ * fused, result cast to the activation dtype. The GEMM stays on the int8
+ * datapath: int32 partial sums per K-group,
+ *   P[m,g,n] = sum_{k in g} a[m,k] * (q[k,n] - 8),
+ *   out[m,n] = a_scale[m] * sum_g w_scale[g,n] * P[m,g,n] + bias[n].
+ *   a         device, int8 [M, K] (codes from w4a8_quantize_act)
+ *   a_scale   device, fp32 [M]
+ *   w_tiled   device, tiled weights from w4_repack (16-byte aligned)
+ *   w_scale   device, [G, N] with G = K/group (1 if group == -1)
+ *   scale_dtype must be W4_F16: [inc_w4a8] notes the int8 kernel reads its
+ *             scales as fp16 whatever the activation dtype and misreads bf16;
+ *             here a bf16 scale is refused instead (W4_ERR_DTYPE)
+ *   group     -1 (one group spanning K: per channel, [ct_w4a8] create_weights,
+ *             [zentorch] can_implement) or a multiple of 64 dividing K
+ *   bias      device or NULL, [N] in out_dtype
+ *   out       device, [M, N] in out_dtype (W4_BF16 or W4_F16)
+ * Errors: INVALID, ALIGN (K or N % 8), GROUP, DTYPE, HIP. M == 0 or N == 0
+ *         enqueues nothing.
+ */
+int w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled,
+              const void* w_scale, int scale_dtype, int64_t group,
+              const void* bias, void* out, int out_dtype,
+              int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Test hook of w4a8_gemm: the same kernel writing the exact int32 per-group
+ * partial sums P[m, g, n] (layout [M, G, N]) instead of the epilogue.
+ * Arguments as w4a8_gemm. Errors as w4a8_gemm.
+ */
+int w4a8_gemm_partials(const int8_t* a, const void* w_tiled, int64_t group,
+                       int32_t* partials, int64_t M, int64_t N, int64_t K,
+                       void* stream);
+
+/*
+ * W4A16 decode GEMM for small batches (M <= 16) on the asymmetric grid
+ * w = (q - 8) * scale + zero.
+ * [cpu_int4] module docstring: single-stream decode is bandwidth-bound; bf16
+ * activations; weights two codes per byte (byte j = w[2j] | w[2j+1] << 4),
+ * bf16 scale and zero per (output row, K-group).
+ *   out[m,n] = sum_k x[m,k] * ((q[n,k] - 8) * scale[n,k/group] + zero[n,k/group])
+ *   x       device, bf16 [M, K] contiguous
+ *   w       device, uint8 [N, K/2] in that byte layout (read as is)
+ *   scale   device, bf16 [N, K/group]
+ *   zero    device or NULL (zero offsets), bf16 [N, K/group]
+ *   sz_dtype must be W4_BF16
+ *   group   a multiple of 64 dividing K
+ *   out     device, bf16 [M, N]
+ * Errors: INVALID, ALIGN (K, N % 8; pointers 16-byte aligned), GROUP, DTYPE,
+ *         UNSUPPORTED (M > 16), HIP.
+ */
+int w4a16_gemm(const void* x, const uint8_t* w, const void* scale, const void* zero,
+               int sz_dtype, int64_t group, void* out,
+               int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Grouped GEMM over routed-expert segments with FP8 activations.
+ * [w4afp8] W4AFP8Config: routed experts hold int4 group-128 weights
+ * (symmetric, zero point 8) and take per-token dynamic FP8 activations.
+ * Routed rows are grouped by expert: rows expert_offsets[e] ..
+ * expert_offsets[e+1]-1 belong to expert e and row r carries token
+ * row_token[r]:
+ *   out[r,n] = a_scale[t] * sum_g w_scale[e,g,n]
+ *              * sum_{k in g} dec(a[t,k]) * (q[e,k,n] - 8),   t = row_token[r]
+ *   a           device, E4M3 codes [T, K] (from w4a8_quantize_act)
+ *   a_scale     device, fp32 [T]
+ *   a_group_sums device, fp32 [T, K/group] (from w4a8_quantize_act, same group)
+ *   row_token   device, int32 [R], each in [0, T)
+ *   expert_offsets device, int32 [E+1], non-decreasing, [0] = 0, [E] = R
+ *   w_tiled     device, E tiled matrices (w4_repack with batch = E)
+ *   w_scale     device, fp16 [E, G, N]
+ *   group       a multiple of 128 dividing K
+ *   out         device, bf16 [R, N], rows in segment order
+ * Errors: INVALID, ALIGN, GROUP, DTYPE, HIP. Offsets and token ids are read
+ * on the device and are not validated; out-of-range values are undefined
+ * behaviour.
+ */
+int w4a8_grouped_gemm(const void* a, int a_dtype, const float* a_scale,
+                      const float* a_group_sums, const int32_t* row_token,
+                      const int32_t* expert_offsets, int64_t E,
+                      const void* w_tiled, const void* w_scale, int scale_dtype,
+                      int64_t group, void* out, int out_dtype,
+                      int64_t T, int64_t R, int64_t N, int64_t K, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* w4_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int w4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4_H */

@@ -1,0 +1,226 @@
+// C ABI of libw4.so (declared in include/w4.h): argument validation, error
+// reporting and kernel launches. Validation runs entirely on the host and
+// touches no HIP API, so a rejected call enqueues nothing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/w4.h"
+#include "w4_device.h"
+
+namespace w4 {
+hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, void* codes,
+                            bool fp8, float* scales, float* gsums, int group, hipStream_t stream);
+size_t tiled_bytes(int64_t K, int64_t N);
+hipError_t launch_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch, void* dst,
+                         hipStream_t stream);
+hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled, const void* w_scale,
+                            int64_t group, const void* bias, void* out, bool out_bf16, int32_t* partials,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_w4a16(const void* x, const uint8_t* w, const void* scale, const void* zero, int64_t group,
+                        void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* gsum, const int32_t* row_token,
+                              const int32_t* offsets, int64_t E, const void* w_tiled, size_t w_bytes_per_expert,
+                              const void* w_scale, int64_t group, void* out, int64_t T, int64_t R, int64_t N,
+                              int64_t K, hipStream_t stream);
+}  // namespace w4
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return W4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(W4_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// Shared checks of the GEMM dimensions: [inc_w4a8] create_weights requires
+// both GEMM dims to be multiples of 8 and names the offending sizes.
+int check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0)
+    return fail(W4_ERR_INVALID, "%s: sizes must be M >= 0, N >= 0, K > 0 (got M=%lld N=%lld K=%lld)", fn,
+                (long long)M, (long long)N, (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > ((int64_t)1 << 24))
+    return fail(W4_ERR_UNSUPPORTED, "%s: sizes too large (M=%lld N=%lld K=%lld)", fn, (long long)M,
+                (long long)N, (long long)K);
+  if (K % 8 || N % 8) {
+    char buf[96] = "";
+    if (K % 8) snprintf(buf, sizeof(buf), "input K=%lld", (long long)K);
+    if (N % 8)
+      snprintf(buf + strlen(buf), sizeof(buf) - strlen(buf), "%soutput N=%lld", (K % 8) ? ", " : "",
+               (long long)N);
+    return fail(W4_ERR_ALIGN, "%s: in/out sizes must be multiples of 8, got %s (shape K=%lld, N=%lld)", fn, buf,
+                (long long)K, (long long)N);
+  }
+  return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4_last_error(void) { return g_err; }
+
+int w4_version(void) { return 100; }
+
+int w4a8_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, void* codes,
+                      int code_dtype, float* scales, float* group_sums, int64_t group, void* stream) {
+  const char* fn = "w4a8_quantize_act";
+  if (M < 0 || K < 0) return fail(W4_ERR_INVALID, "%s: negative size M=%lld K=%lld", fn, (long long)M, (long long)K);
+  if (x_dtype != W4_BF16 && x_dtype != W4_F16)
+    return fail(W4_ERR_DTYPE, "%s: activations must be bf16 or fp16 (dtype code %d)", fn, x_dtype);
+  if (code_dtype != W4_I8 && code_dtype != W4_FP8_E4M3)
+    return fail(W4_ERR_DTYPE, "%s: codes must be int8 or fp8 e4m3 (dtype code %d)", fn, code_dtype);
+  if (K % 8) return fail(W4_ERR_ALIGN, "%s: K=%lld is not a multiple of 8", fn, (long long)K);
+  if (M > kMaxDim || K > ((int64_t)1 << 24))
+    return fail(W4_ERR_UNSUPPORTED, "%s: sizes too large (M=%lld K=%lld)", fn, (long long)M, (long long)K);
+  if (ldx < K || ldx % 8)
+    return fail(W4_ERR_ALIGN, "%s: ldx=%lld must be >= K=%lld and a multiple of 8", fn, (long long)ldx,
+                (long long)K);
+  if (group_sums) {
+    if (code_dtype != W4_FP8_E4M3)
+      return fail(W4_ERR_DTYPE, "%s: group sums are produced for fp8 codes only", fn);
+    const int64_t gc = group / 8;
+    if (group <= 0 || group % 8 || K % group || gc > 64 || (gc & (gc - 1)))
+      return fail(W4_ERR_GROUP, "%s: group sums need group in {8,16,...,512} (power of two) dividing K, got %lld "
+                  "(K=%lld)", fn, (long long)group, (long long)K);
+  }
+  if (M == 0) return ok();
+  if (!x || !codes || !scales) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(x)) return fail(W4_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(codes) & 7u) != 0) return fail(W4_ERR_ALIGN, "%s: codes must be 8-byte aligned", fn);
+  return hip_status(w4::launch_quant_act(x, x_dtype == W4_BF16, M, K, ldx, codes, code_dtype == W4_FP8_E4M3,
+                                         scales, group_sums, (int)(group_sums ? group : 8),
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int w4_repack_bytes(int64_t K, int64_t N, size_t* bytes) {
+  const char* fn = "w4_repack_bytes";
+  if (!bytes) return fail(W4_ERR_INVALID, "%s: null output pointer", fn);
+  int rc = check_mnk(fn, 0, N, K);
+  if (rc) return rc;
+  *bytes = w4::tiled_bytes(K, N);
+  return ok();
+}
+
+int w4_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch, void* dst, void* stream) {
+  const char* fn = "w4_repack";
+  int rc = check_mnk(fn, 0, N, K);
+  if (rc) return rc;
+  if (layout != W4_LAYOUT_GPTQ_KN && layout != W4_LAYOUT_CT_NK && layout != W4_LAYOUT_S4_NK)
+    return fail(W4_ERR_INVALID, "%s: unknown source layout %d", fn, layout);
+  if (batch < 0 || batch > 65535) return fail(W4_ERR_INVALID, "%s: batch=%lld out of range", fn, (long long)batch);
+  if (batch == 0 || N == 0) return ok();
+  if (!src || !dst) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(dst)) return fail(W4_ERR_ALIGN, "%s: dst must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(src) & 3u) != 0) return fail(W4_ERR_ALIGN, "%s: src must be 4-byte aligned", fn);
+  return hip_status(w4::launch_repack(src, layout, K, N, batch, dst, static_cast<hipStream_t>(stream)), fn);
+}
+
+static int check_gemm(const char* fn, const int8_t* a, const void* w_tiled, int64_t group, int64_t M, int64_t N,
+                      int64_t K) {
+  int rc = check_mnk(fn, M, N, K);
+  if (rc) return rc;
+  if (group != -1 && (group <= 0 || group % 64 || K % group))
+    return fail(W4_ERR_GROUP, "%s: group size %lld must be -1 (per channel) or a multiple of 64 dividing K=%lld", fn,
+                (long long)group, (long long)K);
+  if (M == 0 || N == 0) return W4_OK;
+  if (!a || !w_tiled) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(w_tiled)) return fail(W4_ERR_ALIGN, "%s: w_tiled must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(a) & 7u) != 0) return fail(W4_ERR_ALIGN, "%s: a must be 8-byte aligned", fn);
+  return W4_OK;
+}
+
+int w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled, const void* w_scale, int scale_dtype,
+              int64_t group, const void* bias, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+              void* stream) {
+  const char* fn = "w4a8_gemm";
+  if (scale_dtype != W4_F16)
+    return fail(W4_ERR_DTYPE, "%s: weight scales must be fp16 (dtype code %d); the int8 kernel reads them as fp16",
+                fn, scale_dtype);
+  if (out_dtype != W4_BF16 && out_dtype != W4_F16)
+    return fail(W4_ERR_DTYPE, "%s: output must be bf16 or fp16 (dtype code %d)", fn, out_dtype);
+  int rc = check_gemm(fn, a, w_tiled, group, M, N, K);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return ok();
+  if (!a_scale || !w_scale || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  return hip_status(w4::launch_w4a8_gemm(a, a_scale, w_tiled, w_scale, group, bias, out, out_dtype == W4_BF16,
+                                         nullptr, M, N, K, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int w4a8_gemm_partials(const int8_t* a, const void* w_tiled, int64_t group, int32_t* partials, int64_t M, int64_t N,
+                       int64_t K, void* stream) {
+  const char* fn = "w4a8_gemm_partials";
+  int rc = check_gemm(fn, a, w_tiled, group, M, N, K);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return ok();
+  if (!partials) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  return hip_status(w4::launch_w4a8_gemm(a, nullptr, w_tiled, nullptr, group, nullptr, nullptr, true, partials, M, N,
+                                         K, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int w4a16_gemm(const void* x, const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group,
+               void* out, int64_t M, int64_t N, int64_t K, void* stream) {
+  const char* fn = "w4a16_gemm";
+  if (sz_dtype != W4_BF16) return fail(W4_ERR_DTYPE, "%s: scale and zero must be bf16 (dtype code %d)", fn, sz_dtype);
+  int rc = check_mnk(fn, M, N, K);
+  if (rc) return rc;
+  if (group <= 0 || group % 64 || K % group)
+    return fail(W4_ERR_GROUP, "%s: group size %lld must be a multiple of 64 dividing K=%lld", fn, (long long)group,
+                (long long)K);
+  if (M > 16) return fail(W4_ERR_UNSUPPORTED, "%s: M=%lld > 16 (decode kernel handles up to 16 rows)", fn, (long long)M);
+  if (M == 0 || N == 0) return ok();
+  if (!x || !w || !scale || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(x) || !aligned16(w))
+    return fail(W4_ERR_ALIGN, "%s: x and w must be 16-byte aligned", fn);
+  return hip_status(w4::launch_w4a16(x, w, scale, zero, group, out, M, N, K, static_cast<hipStream_t>(stream)), fn);
+}
+
+int w4a8_grouped_gemm(const void* a, int a_dtype, const float* a_scale, const float* a_group_sums,
+                      const int32_t* row_token, const int32_t* expert_offsets, int64_t E, const void* w_tiled,
+                      const void* w_scale, int scale_dtype, int64_t group, void* out, int out_dtype, int64_t T,
+                      int64_t R, int64_t N, int64_t K, void* stream) {
+  const char* fn = "w4a8_grouped_gemm";
+  if (a_dtype != W4_FP8_E4M3) return fail(W4_ERR_DTYPE, "%s: activations must be fp8 e4m3 (dtype code %d)", fn, a_dtype);
+  if (scale_dtype != W4_F16) return fail(W4_ERR_DTYPE, "%s: weight scales must be fp16 (dtype code %d)", fn, scale_dtype);
+  if (out_dtype != W4_BF16) return fail(W4_ERR_DTYPE, "%s: output must be bf16 (dtype code %d)", fn, out_dtype);
+  int rc = check_mnk(fn, R, N, K);
+  if (rc) return rc;
+  if (E < 0 || E > 65535 || T < 0) return fail(W4_ERR_INVALID, "%s: E=%lld T=%lld out of range", fn, (long long)E, (long long)T);
+  const int64_t gt = group / 128;
+  if (group <= 0 || group % 128 || K % group || gt > 4 || (gt & (gt - 1)))
+    return fail(W4_ERR_GROUP, "%s: group size %lld must be 128, 256 or 512 and divide K=%lld", fn, (long long)group,
+                (long long)K);
+  if (R == 0 || N == 0 || E == 0) return ok();
+  if (T <= 0 || (int64_t)T * K >= ((int64_t)1 << 35))
+    return fail(W4_ERR_UNSUPPORTED, "%s: token count T=%lld out of range for K=%lld", fn, (long long)T, (long long)K);
+  if (!a || !a_scale || !a_group_sums || !row_token || !expert_offsets || !w_tiled || !w_scale || !out)
+    return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(a) || !aligned16(w_tiled)) return fail(W4_ERR_ALIGN, "%s: a and w_tiled must be 16-byte aligned", fn);
+  return hip_status(w4::launch_grouped_fp8(a, a_scale, a_group_sums, row_token, expert_offsets, E, w_tiled,
+                                           w4::tiled_bytes(K, N), w_scale, group, out, T, R, N, K,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

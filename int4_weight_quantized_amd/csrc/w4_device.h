@@ -1,0 +1,73 @@
+// Device-side helpers shared by the gfx950 kernels of libw4.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+namespace w4 {
+
+constexpr int kWave = 64;
+
+// Kernel-tiled int4 weight layout (written by w4_repack, read by the GEMMs):
+// tiles of kTileN output columns x kTileK K-values, 8 KiB each, ordered
+// [n_tile][k_tile]. Inside a tile, 16-byte unit u = n_local*4 + kq holds the
+// 32 codes of column n_local for k = 32*kq .. 32*kq+31: in word j (0..3),
+// byte b (0..3), the low nibble is the code of k = 32*kq + 4*j + b and the
+// high nibble the code of k + 16. Nibbles are stored as q ^ 8, the
+// two's-complement int4 of q - 8, so (w & 0xF0F0F0F0) and ((w << 4) &
+// 0xF0F0F0F0) are int8 bytes equal to 16*(q - 8) in K order.
+constexpr int kTileN = 128;
+constexpr int kTileK = 128;
+constexpr int kTileBytes = kTileN * kTileK / 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // gfx9 raw buffer: stride 0, num_records in bytes; accesses past the end
+  // return zero instead of faulting.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ v4i buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  // round to nearest even; inputs here are finite
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);   // IEEE conversion, nearest even
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Map a linear block id to a tile id so that blocks the hardware sends to
+// the same XCD (round-robin over 8 XCDs) get a contiguous run of tile ids.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  if (nblocks % kXcd != 0) return bid;
+  return (bid % kXcd) * (nblocks / kXcd) + bid / kXcd;
+}
+
+}  // namespace w4

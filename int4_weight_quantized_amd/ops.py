@@ -1,0 +1,173 @@
+"""ctypes binding of libw4.so: one Python function per C entry point, same
+names, argument marshalling only (torch tensors -> device pointers, dtype
+codes, the current HIP stream). Every step runs in the HIP library; there
+is no fallback. A missing library or a failed call raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4.so")
+
+W4_BF16, W4_F16, W4_F32, W4_I8, W4_FP8_E4M3 = 1, 2, 3, 4, 5
+W4_LAYOUT_GPTQ_KN, W4_LAYOUT_CT_NK, W4_LAYOUT_S4_NK = 1, 2, 3
+ERRORS = {0: "OK", -1: "INVALID", -2: "ALIGN", -3: "GROUP", -4: "DTYPE", -5: "UNSUPPORTED", -6: "HIP"}
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+
+_SIGS = {
+    "w4a8_quantize_act": [_P, _I, _I64, _I64, _I64, _P, _I, _P, _P, _I64, _P],
+    "w4_repack_bytes": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+    "w4_repack": [_P, _I, _I64, _I64, _I64, _P, _P],
+    "w4a8_gemm": [_P, _P, _P, _P, _I, _I64, _P, _P, _I, _I64, _I64, _I64, _P],
+    "w4a8_gemm_partials": [_P, _P, _I64, _P, _I64, _I64, _I64, _P],
+    "w4a16_gemm": [_P, _P, _P, _P, _I, _I64, _P, _I64, _I64, _I64, _P],
+    "w4a8_grouped_gemm": [_P, _I, _P, _P, _P, _P, _I64, _P, _P, _I, _I64, _P, _I, _I64, _I64, _I64, _I64, _P],
+    "w4_last_error": [],
+    "w4_version": [],
+}
+
+
+class W4Error(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {ERRORS.get(code, code)} ({code}): {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4.so (built in-tree by build.py). Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with int4_weight_quantized_amd/build.py "
+                               "(or __graft_entry__.build()); there is no fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name == "w4_last_error" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise W4Error(fn, rc, lib().w4_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream=None) -> int | None:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def _half_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return W4_BF16
+    if dt == torch.float16:
+        return W4_F16
+    raise TypeError(f"unsupported half dtype {dt}")
+
+
+# ----------------------------------------------------------------- entry points
+
+def w4a8_quantize_act(x: torch.Tensor, code_dtype: str = "i8", group_sums_group: int | None = None,
+                      stream=None):
+    """x [M, K] bf16/fp16 -> (codes [M, K] int8 or uint8 E4M3 bits, scales fp32 [M],
+    group_sums fp32 [M, K/group] or None)."""
+    M, K = x.shape
+    fp8 = code_dtype == "fp8"
+    codes = torch.empty((M, K), dtype=torch.uint8 if fp8 else torch.int8, device=x.device)
+    scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    gs = None
+    if group_sums_group is not None:
+        gs = torch.empty((M, K // group_sums_group), dtype=torch.float32, device=x.device)
+    quantize_act_into(x, codes, scales, gs, group_sums_group or 0, fp8, stream)
+    return codes, scales, gs
+
+
+def quantize_act_into(x, codes, scales, group_sums=None, group=0, fp8=False, stream=None):
+    M, K = x.shape
+    _check("w4a8_quantize_act", lib().w4a8_quantize_act(
+        _ptr(x), _half_code(x.dtype), M, K, K, _ptr(codes), W4_FP8_E4M3 if fp8 else W4_I8,
+        _ptr(scales), _ptr(group_sums), group, _stream(stream)))
+
+
+def w4_repack_bytes(K: int, N: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("w4_repack_bytes", lib().w4_repack_bytes(K, N, ctypes.byref(n)))
+    return n.value
+
+
+def w4_repack(src: torch.Tensor, layout: int, K: int, N: int, batch: int = 1, stream=None) -> torch.Tensor:
+    """Repack `batch` int4 matrices into the kernel-tiled layout (uint8 buffer)."""
+    nbytes = w4_repack_bytes(K, N)
+    dst = torch.empty((batch, nbytes), dtype=torch.uint8, device=src.device)
+    _check("w4_repack", lib().w4_repack(_ptr(src), layout, K, N, batch, _ptr(dst), _stream(stream)))
+    return dst
+
+
+def w4a8_gemm(a, a_scale, w_tiled, w_scale, group: int, N: int, out_dtype=torch.bfloat16, bias=None,
+              out=None, stream=None):
+    M, K = a.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    sdt = W4_F16 if w_scale.dtype == torch.float16 else (W4_BF16 if w_scale.dtype == torch.bfloat16 else W4_F32)
+    _check("w4a8_gemm", lib().w4a8_gemm(
+        _ptr(a), _ptr(a_scale), _ptr(w_tiled), _ptr(w_scale), sdt, group, _ptr(bias), _ptr(out),
+        _half_code(out.dtype), M, N, K, _stream(stream)))
+    return out
+
+
+def w4a8_gemm_partials(a, w_tiled, group: int, N: int, stream=None):
+    M, K = a.shape
+    G = 1 if group == -1 else K // group
+    P = torch.empty((M, G, N), dtype=torch.int32, device=a.device)
+    _check("w4a8_gemm_partials", lib().w4a8_gemm_partials(
+        _ptr(a), _ptr(w_tiled), group, _ptr(P), M, N, K, _stream(stream)))
+    return P
+
+
+def w4a16_gemm(x, w, scale, zero, group: int, out=None, stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check("w4a16_gemm", lib().w4a16_gemm(
+        _ptr(x), _ptr(w), _ptr(scale), _ptr(zero), _half_code(scale.dtype), group, _ptr(out),
+        M, N, K, _stream(stream)))
+    return out
+
+
+def w4a8_grouped_gemm(a8, a_scale, a_group_sums, row_token, expert_offsets, w_tiled, w_scale,
+                      group: int, N: int, out=None, stream=None):
+    T, K = a8.shape
+    R = row_token.shape[0]
+    E = expert_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=a8.device)
+    _check("w4a8_grouped_gemm", lib().w4a8_grouped_gemm(
+        _ptr(a8), W4_FP8_E4M3, _ptr(a_scale), _ptr(a_group_sums), _ptr(row_token), _ptr(expert_offsets),
+        E, _ptr(w_tiled), _ptr(w_scale), W4_F16, group, _ptr(out), W4_BF16, T, R, N, K, _stream(stream)))
+    return out
+
+
+def w4_version() -> int:
+    return lib().w4_version()

@@ -1,0 +1,90 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU (argument
+validation runs on the host and enqueues nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(w4\w*)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from int4_weight_quantized_amd import ops
+    if not os.path.exists(ops.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ops.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ("w4a8_quantize_act", "w4a8_gemm", "w4a16_gemm", "w4a8_grouped_gemm", "w4_repack",
+                 "w4_repack_bytes", "w4a8_gemm_partials", "w4_last_error", "w4_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert L.w4_version() == 100
+
+
+def _err(L):
+    return L.w4_last_error().decode()
+
+
+def test_dim_alignment_errors_name_the_sizes(L):
+    # both GEMM dims must be multiples of 8; the message names the offender
+    rc = L.w4a8_gemm(None, None, None, None, 2, 128, None, None, 1, 16, 256, 200 + 4, None)
+    assert rc == -2 and "input K=204" in _err(L)
+    rc = L.w4a8_gemm(None, None, None, None, 2, -1, None, None, 1, 16, 260, 256, None)
+    assert rc == -2 and "output N=260" in _err(L)
+
+
+def test_scale_dtype_rule(L):
+    # bf16 scales would be misread by an fp16-reading kernel: refused
+    rc = L.w4a8_gemm(None, None, None, None, 1, 128, None, None, 1, 16, 256, 256, None)
+    assert rc == -4 and "fp16" in _err(L)
+
+
+def test_group_rules(L):
+    assert L.w4a8_gemm(None, None, None, None, 2, 96, None, None, 1, 16, 256, 288, None) == -3
+    assert L.w4a8_gemm(None, None, None, None, 2, 128, None, None, 1, 16, 256, 192, None) == -3
+    assert L.w4a16_gemm(None, None, None, None, 1, 48, None, 1, 256, 256, None) == -3
+    assert L.w4a8_grouped_gemm(None, 5, None, None, None, None, 4, None, None, 2, 64, None, 1,
+                               8, 8, 256, 256, None) == -3
+
+
+def test_null_and_negative(L):
+    assert L.w4a8_gemm(None, None, None, None, 2, 128, None, None, 1, 16, 256, 256, None) == -1
+    assert L.w4a8_quantize_act(None, 1, -1, 256, 256, None, 4, None, None, 0, None) == -1
+    assert L.w4a8_gemm(None, None, None, None, 2, 128, None, None, 1, 16, 256, 0, None) == -1
+
+
+def test_empty_inputs_are_noops(L):
+    # M == 0 (or N == 0) enqueues nothing and succeeds even with null buffers
+    assert L.w4a8_gemm(None, None, None, None, 2, 128, None, None, 1, 0, 256, 256, None) == 0
+    assert L.w4a8_quantize_act(None, 1, 0, 256, 256, None, 4, None, None, 0, None) == 0
+    assert L.w4a16_gemm(None, None, None, None, 1, 64, None, 0, 256, 256, None) == 0
+
+
+def test_decode_batch_limit(L):
+    assert L.w4a16_gemm(None, None, None, None, 1, 64, None, 17, 256, 256, None) == -5
+
+
+def test_repack_bytes(L):
+    n = ctypes.c_size_t()
+    assert L.w4_repack_bytes(4096, 14336, ctypes.byref(n)) == 0
+    assert n.value == 4096 * 14336 // 2
+    assert L.w4_repack_bytes(200, 8, ctypes.byref(n)) == 0
+    assert n.value == 2 * 1 * 8192               # padded to 128 x 128 tiles
