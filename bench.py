@@ -148,10 +148,10 @@ def main():
             base_w = torch.from_numpy(dd["w"]).to(dev)
             base_s = dev_half(dd["scale"], "bf16")
             base_z = dev_half(dd["zero"], "bf16")
-            sets = [(base_w.roll(i, 0).contiguous(), base_s.roll(i, 0).contiguous(),
-                     base_z.roll(i, 0).contiguous()) for i in range(nrot)]
+            sets = [ops.w4a16_repack(base_w.roll(i, 0).contiguous(), base_s.roll(i, 0).contiguous(),
+                                     base_z.roll(i, 0).contiguous(), gd) for i in range(nrot)]
             yd = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
-            calls = [(lambda st=st: ops.w4a16_gemm(xd, st[0], st[1], st[2], gd, out=yd)) for st in sets]
+            calls = [(lambda st=st: ops.w4a16_gemm(xd, st[0], st[1], gd, Nd, out=yd)) for st in sets]
             reps = max(1, args.steps // 4)
             per, _, _ = timed(calls, reps, max(1, args.warmup // 4))
             t = float(np.mean(per))

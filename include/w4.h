@@ -156,24 +156,32 @@ int w4a8_gemm_partials(const int8_t* a, const void* w_tiled, int64_t group,
                        void* stream);
 
 /*
- * W4A16 decode GEMM for small batches (M <= 16) on the asymmetric grid
- * w = (q - 8) * scale + zero.
+ * W4A16 decode path (M <= 16) on the asymmetric grid w = (q - 8) * scale + zero.
  * [cpu_int4] module docstring: single-stream decode is bandwidth-bound; bf16
  * activations; weights two codes per byte (byte j = w[2j] | w[2j+1] << 4),
- * bf16 scale and zero per (output row, K-group).
+ * bf16 scale and zero per (output row, K-group); the weights are repacked
+ * once at load time into the layout the kernel streams (as that page does
+ * for its own kernel).
+ *
+ * w4a16_repack_bytes: sizes of the two tiled buffers for a [N, K] matrix.
+ * w4a16_repack: load-time repack.
+ *   w        device, uint8 [N, K/2] in the byte layout above
+ *   scale    device, bf16 [N, K/group];  zero: device bf16 [N, K/group] or
+ *            NULL (zero offsets);  sz_dtype must be W4_BF16
+ *   group    64, 128, 256 or 512, dividing K
+ *   w_tiled  device, w_bytes (16-byte aligned); sz_tiled: device, sz_bytes
+ * w4a16_gemm:
  *   out[m,n] = sum_k x[m,k] * ((q[n,k] - 8) * scale[n,k/group] + zero[n,k/group])
- *   x       device, bf16 [M, K] contiguous
- *   w       device, uint8 [N, K/2] in that byte layout (read as is)
- *   scale   device, bf16 [N, K/group]
- *   zero    device or NULL (zero offsets), bf16 [N, K/group]
- *   sz_dtype must be W4_BF16
- *   group   a multiple of 64 dividing K
- *   out     device, bf16 [M, N]
- * Errors: INVALID, ALIGN (K, N % 8; pointers 16-byte aligned), GROUP, DTYPE,
- *         UNSUPPORTED (M > 16), HIP.
+ *   x        device, bf16 [M, K] contiguous (16-byte aligned)
+ *   w_tiled, sz_tiled  from w4a16_repack with the same K, N, group
+ *   out      device, bf16 [M, N]
+ * Errors: INVALID, ALIGN (K, N % 8; pointers), GROUP, DTYPE,
+ *         UNSUPPORTED (M > 16, N*K >= 2^31), HIP.
  */
-int w4a16_gemm(const void* x, const uint8_t* w, const void* scale, const void* zero,
-               int sz_dtype, int64_t group, void* out,
+int w4a16_repack_bytes(int64_t K, int64_t N, int64_t group, size_t* w_bytes, size_t* sz_bytes);
+int w4a16_repack(const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group,
+                 int64_t K, int64_t N, void* w_tiled, void* sz_tiled, void* stream);
+int w4a16_gemm(const void* x, const void* w_tiled, const void* sz_tiled, int64_t group, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);
 
 /*

@@ -17,8 +17,11 @@ hipError_t launch_repack(const void* src, int layout, int64_t K, int64_t N, int6
 hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled, const void* w_scale,
                             int64_t group, const void* bias, void* out, bool out_bf16, int32_t* partials,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
-hipError_t launch_w4a16(const void* x, const uint8_t* w, const void* scale, const void* zero, int64_t group,
-                        void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+void w4a16_tiled_bytes(int64_t K, int64_t N, size_t* wbytes, size_t* szbytes);
+hipError_t launch_w4a16_repack(const uint8_t* w, const void* scale, const void* zero, int64_t group, int64_t K,
+                               int64_t N, void* w_tiled, void* sz_tiled, hipStream_t stream);
+hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled, int64_t group, void* out,
+                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* gsum, const int32_t* row_token,
                               const int32_t* offsets, int64_t E, const void* w_tiled, size_t w_bytes_per_expert,
                               const void* w_scale, int64_t group, void* out, int64_t T, int64_t R, int64_t N,
@@ -179,21 +182,54 @@ int w4a8_gemm_partials(const int8_t* a, const void* w_tiled, int64_t group, int3
                     fn);
 }
 
-int w4a16_gemm(const void* x, const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group,
-               void* out, int64_t M, int64_t N, int64_t K, void* stream) {
-  const char* fn = "w4a16_gemm";
-  if (sz_dtype != W4_BF16) return fail(W4_ERR_DTYPE, "%s: scale and zero must be bf16 (dtype code %d)", fn, sz_dtype);
-  int rc = check_mnk(fn, M, N, K);
+static int check_w4a16(const char* fn, int64_t group, int64_t N, int64_t K) {
+  int rc = check_mnk(fn, 0, N, K);
   if (rc) return rc;
-  if (group <= 0 || group % 64 || K % group)
-    return fail(W4_ERR_GROUP, "%s: group size %lld must be a multiple of 64 dividing K=%lld", fn, (long long)group,
-                (long long)K);
+  if (group != 64 && group != 128 && group != 256 && group != 512)
+    return fail(W4_ERR_GROUP, "%s: group size %lld must be 64, 128, 256 or 512", fn, (long long)group);
+  if (K % group) return fail(W4_ERR_GROUP, "%s: group size %lld does not divide K=%lld", fn, (long long)group, (long long)K);
+  size_t wb, sb;
+  w4::w4a16_tiled_bytes(K, N, &wb, &sb);
+  if (wb >= ((size_t)1 << 31) || (uint64_t)N * (uint64_t)K >= ((uint64_t)1 << 31))
+    return fail(W4_ERR_UNSUPPORTED, "%s: weight matrix too large (N=%lld K=%lld)", fn, (long long)N, (long long)K);
+  return W4_OK;
+}
+
+int w4a16_repack_bytes(int64_t K, int64_t N, int64_t group, size_t* w_bytes, size_t* sz_bytes) {
+  const char* fn = "w4a16_repack_bytes";
+  if (!w_bytes || !sz_bytes) return fail(W4_ERR_INVALID, "%s: null output pointer", fn);
+  int rc = check_w4a16(fn, group, N, K);
+  if (rc) return rc;
+  w4::w4a16_tiled_bytes(K, N, w_bytes, sz_bytes);
+  return ok();
+}
+
+int w4a16_repack(const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group, int64_t K,
+                 int64_t N, void* w_tiled, void* sz_tiled, void* stream) {
+  const char* fn = "w4a16_repack";
+  if (sz_dtype != W4_BF16) return fail(W4_ERR_DTYPE, "%s: scale and zero must be bf16 (dtype code %d)", fn, sz_dtype);
+  int rc = check_w4a16(fn, group, N, K);
+  if (rc) return rc;
+  if (N == 0) return ok();
+  if (!w || !scale || !w_tiled || !sz_tiled) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(w_tiled) || !aligned16(sz_tiled))
+    return fail(W4_ERR_ALIGN, "%s: w_tiled and sz_tiled must be 16-byte aligned", fn);
+  return hip_status(w4::launch_w4a16_repack(w, scale, zero, group, K, N, w_tiled, sz_tiled,
+                                            static_cast<hipStream_t>(stream)), fn);
+}
+
+int w4a16_gemm(const void* x, const void* w_tiled, const void* sz_tiled, int64_t group, void* out, int64_t M,
+               int64_t N, int64_t K, void* stream) {
+  const char* fn = "w4a16_gemm";
+  if (M < 0) return fail(W4_ERR_INVALID, "%s: negative M=%lld", fn, (long long)M);
+  int rc = check_w4a16(fn, group, N, K);
+  if (rc) return rc;
   if (M > 16) return fail(W4_ERR_UNSUPPORTED, "%s: M=%lld > 16 (decode kernel handles up to 16 rows)", fn, (long long)M);
   if (M == 0 || N == 0) return ok();
-  if (!x || !w || !scale || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
-  if (!aligned16(x) || !aligned16(w))
-    return fail(W4_ERR_ALIGN, "%s: x and w must be 16-byte aligned", fn);
-  return hip_status(w4::launch_w4a16(x, w, scale, zero, group, out, M, N, K, static_cast<hipStream_t>(stream)), fn);
+  if (!x || !w_tiled || !sz_tiled || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(sz_tiled))
+    return fail(W4_ERR_ALIGN, "%s: x, w_tiled and sz_tiled must be 16-byte aligned", fn);
+  return hip_status(w4::launch_w4a16(x, w_tiled, sz_tiled, group, out, M, N, K, static_cast<hipStream_t>(stream)), fn);
 }
 
 int w4a8_grouped_gemm(const void* a, int a_dtype, const float* a_scale, const float* a_group_sums,

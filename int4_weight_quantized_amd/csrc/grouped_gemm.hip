@@ -30,11 +30,14 @@ constexpr int kEStageA = kEM * kEK, kEStageB = kEN * kEK, kEStage = kEStageA + k
 
 __device__ __forceinline__ int eswz(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
 
+// GT: K steps (of 128) per weight group (group = 128 * GT)
+template <int GT>
 __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ a_scale, const float* __restrict__ gsum,
     const int32_t* __restrict__ row_token, const int32_t* __restrict__ offsets, int E,
     const v4i* __restrict__ Wt, int64_t w_stride16, const uint16_t* __restrict__ wscale,
-    int group_tiles, uint16_t* __restrict__ out, int N, int K, int KT, int NT) {
+    uint16_t* __restrict__ out, int N, int K, int KT, int NT) {
+  constexpr int group_tiles = GT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kEStage];
   __shared__ int s_tok[kEM];                       // token of each row of the tile (-1: none)
   __shared__ __attribute__((aligned(16))) float s_gs[2][kEM];   // -8 * row sum of the staged group
@@ -67,28 +70,24 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   if (tid < kEM) s_tok[tid] = (r0 + tid < cnt) ? row_token[seg0 + r0 + tid] : -1;
   __syncthreads();
   const int arow0 = tid >> 3, akc = tid & 7;
-  uint32_t aoff[4];                        // byte offset of the row's token / 16; ~0u: no row
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tk_ = s_tok[arow0 + 32 * i];
-    aoff[i] = (tk_ >= 0) ? (uint32_t)(((int64_t)tk_ * K) >> 4) : ~0u;
-  }
   const uint8_t* abase = A + 16 * akc;
   const v4i* wexp = Wt + (int64_t)e * w_stride16;
   v4i pa[4], pb[2];
   float pgs = 0.f;
   auto gload = [&](int tk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pa[i] = (aoff[i] != ~0u)
-                  ? *reinterpret_cast<const v4i*>(abase + ((int64_t)aoff[i] << 4) + (int64_t)tk * kEK)
-                  : v4i{0, 0, 0, 0};
+    for (int i = 0; i < 4; ++i) {
+      const int tk_ = s_tok[arow0 + 32 * i];          // LDS read: no live register per row
+      const v4i v = *reinterpret_cast<const v4i*>(abase + (int64_t)max(tk_, 0) * K + (int64_t)tk * kEK);
+      pa[i] = (tk_ >= 0) ? v : v4i{0, 0, 0, 0};
+    }
     const v4i* wt = wexp + (((int64_t)tn * KT + tk) << 9);
     pb[0] = wt[tid];
     pb[1] = wt[tid + kEThreads];
     if (tid < kEM && (tk % group_tiles) == 0) {
       const int tk_ = s_tok[tid];
-      pgs = (tk_ >= 0) ? -8.f * gsum[(int64_t)tk_ * G + tk / group_tiles] : 0.f;
+      const float v = gsum[(int64_t)max(tk_, 0) * G + tk / group_tiles];   // clamped: no branch
+      pgs = (tk_ >= 0) ? -8.f * v : 0.f;
     }
   };
   auto lstore = [&](int stage, int tk) {
@@ -113,9 +112,14 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   };
 
   // ---- per-lane output rows / columns
-  int ncol[4];
+  const int ncol0 = n0 + 64 * wn + (lane & 15);    // column of fragment j: ncol0 + 16 j
+  // scales of the group that ends in a K step, fetched one step ahead
+  uint16_t scr[4];
+  auto fetch_scales = [&](int tk) {
+    const int g = tk / group_tiles;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ncol[j] = n0 + 64 * wn + 16 * j + (lane & 15);
+    for (int j = 0; j < 4; ++j) scr[j] = wscale[((int64_t)e * G + g) * N + min(ncol0 + 16 * j, N - 1)];
+  };
   v4f acc[4][4];
   float facc[4][4][4];
 #pragma unroll
@@ -126,20 +130,20 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       for (int r = 0; r < 4; ++r) facc[i][j][r] = 0.f;
 
   gload(0);
+  fetch_scales(0);
   lstore(0, 0);
   __syncthreads();
   for (int tk = 0; tk < KT; ++tk) {
     const int stage = tk & 1;
     const bool more = tk + 1 < KT;
-    if (more) gload(tk + 1);
-    const int g = tk / group_tiles;
     const bool fresh = (tk % group_tiles) == 0;
     const bool last = (tk % group_tiles) == group_tiles - 1;
     float sc[4];
-    if (last) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sc[j] = (ncol[j] < N) ? f16_to_f32(wscale[((int64_t)e * G + g) * N + ncol[j]]) : 0.f;
+    for (int j = 0; j < 4; ++j) sc[j] = f16_to_f32(scr[j]);
+    if (more) {
+      gload(tk + 1);
+      fetch_scales(tk + 1);
     }
     const uint8_t* la = lds + stage * kEStage;
     const uint8_t* lb = la + kEStageA;
@@ -152,20 +156,30 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       const v4i x1 = *reinterpret_cast<const v4i*>(lb + eswz(row, kc + 1));
       bf[j] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
-    // group's gsum was staged in s_gs[stage of the group's first K step]
-    const int gs_stage = (tk - (tk % group_tiles)) & 1;
+    if (fresh) {
+      // first K step of a group: the accumulator starts at -8 * row sum
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 64 * wm + 16 * i + (lane & 15);
-      const v4i x0 = *reinterpret_cast<const v4i*>(la + eswz(row, kc));
-      const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 1));
-      const v8i af = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      v4f cinit = {0.f, 0.f, 0.f, 0.f};
-      if (fresh) cinit = *reinterpret_cast<const v4f*>(&s_gs[gs_stage][64 * wm + 16 * i + 4 * (lane >> 4)]);
+      for (int i = 0; i < 4; ++i) {
+        const int row = 64 * wm + 16 * i + (lane & 15);
+        const v4i x0 = *reinterpret_cast<const v4i*>(la + eswz(row, kc));
+        const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 1));
+        const v8i af = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const v4f cinit = *reinterpret_cast<const v4f*>(&s_gs[stage][64 * wm + 16 * i + 4 * (lane >> 4)]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            af, bf[j], fresh ? cinit : acc[i][j], 0, 0, 0, 127, 0, 136);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], cinit, 0, 0, 0, 127, 0, 136);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 64 * wm + 16 * i + (lane & 15);
+        const v4i x0 = *reinterpret_cast<const v4i*>(la + eswz(row, kc));
+        const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 1));
+        const v8i af = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 127, 0, 136);
+      }
     }
     if (last) {
 #pragma unroll
@@ -190,7 +204,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       const float sa = a_scale[tk_];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (ncol[j] < N) out[(int64_t)rr * N + ncol[j]] = f32_to_bf16_rne(facc[i][j][r] * sa);
+        if (ncol0 + 16 * j < N) out[(int64_t)rr * N + ncol0 + 16 * j] = f32_to_bf16_rne(facc[i][j][r] * sa);
     }
 }
 
@@ -204,10 +218,19 @@ hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* 
   const int KT = (int)(K / kEK), NT = (int)((N + kEN - 1) / kEN);
   const int64_t upper = ((R + kEM - 1) / kEM + E) * NT;
   dim3 grid((unsigned)upper), block(kEThreads);
-  hipLaunchKernelGGL(grouped_fp8_kernel, grid, block, 0, stream, static_cast<const uint8_t*>(a), a_scale,
-                     gsum, row_token, offsets, (int)E, static_cast<const v4i*>(w_tiled),
-                     (int64_t)(w_bytes_per_expert / 16), static_cast<const uint16_t*>(w_scale),
-                     (int)(group / kEK), static_cast<uint16_t*>(out), (int)N, (int)K, KT, NT);
+  auto Ap = static_cast<const uint8_t*>(a);
+  auto Wp = static_cast<const v4i*>(w_tiled);
+  auto Sp = static_cast<const uint16_t*>(w_scale);
+  auto Op = static_cast<uint16_t*>(out);
+  const int64_t ws = (int64_t)(w_bytes_per_expert / 16);
+  switch (group / kEK) {
+    case 1: hipLaunchKernelGGL((grouped_fp8_kernel<1>), grid, block, 0, stream, Ap, a_scale, gsum, row_token, offsets,
+                               (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT); break;
+    case 2: hipLaunchKernelGGL((grouped_fp8_kernel<2>), grid, block, 0, stream, Ap, a_scale, gsum, row_token, offsets,
+                               (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT); break;
+    default: hipLaunchKernelGGL((grouped_fp8_kernel<4>), grid, block, 0, stream, Ap, a_scale, gsum, row_token, offsets,
+                                (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT); break;
+  }
   return hipGetLastError();
 }
 

@@ -3,35 +3,49 @@
 // Per the cpu_int4.py page (module docstring, pack_nibbles): single-stream
 // decode is bound by the bytes of the weights read per token; bf16
 // activations; two codes per byte, byte j = w[2j] | w[2j+1] << 4; bf16
-// scale and zero per (output row, group of K).
+// scale and zero per (output row, group of K). Like that page's own kernel
+// layout, the weights are repacked once at load time into the layout the
+// kernel streams.
 //
 //   out[m,n] = sum_g ( scale[n,g] * sum_{k in g} x[m,k]*(q[n,k]-8)
 //                    + zero[n,g]  * sum_{k in g} x[m,k] )
 //
-// Design (gfx950): v_mfma_f32_16x16x32_bf16 with the activations as the
-// 16-row A operand (rows >= M are zero) and 16 weight rows as the B operand.
-// The weights are read in their byte layout as-is: per 64-wide K unit a lane
-// loads 8 bytes (16 codes) of one weight row, so every MFMA step stays inside
-// one scale group. Codes become bf16 values 128+q, exact, with one mask-or
-// (0x4300 | q is the bf16 bit pattern of 128+q), the pairing of K inside
-// the operand being matched by a byte permute of the activations. The row
-// sums sum_k x[m,k] come from the same MFMA against a ones operand, so
-//   sum_k x*(q-8) = C - 136*XS   and   y_g = scale*C + (zero - 136*scale)*XS.
-// Each block owns 16 output columns and splits K across its four waves
-// (whole groups per wave); partial 16x16 tiles are summed through LDS.
-// HBM-bound: 0.5 byte per weight + 4 bytes of scale/zero per group.
+// Tiled layout (w4a16_repack): 16-row tiles x 512-wide K windows.
+//   weights  [row tile][window] 4 KiB: four 1 KiB unit pairs; in a pair, lane
+//            l = n + 16 j (n: row in tile, j: 0..3) owns 16 bytes: 8 bytes of
+//            unit 2p then 8 of unit 2p+1 (a unit is 64 K); each 8 bytes are
+//            two words for K = 16 j + 0..7 and 16 j + 8..15 of the unit, in a
+//            word nibble i < 4 holds K offset 2i and nibble i >= 4 offset
+//            2(i-4)+1. Padding codes are 8.
+//   scale/zero [row tile][window][row 16][8 group slots][scale, zero] bf16
+//            (slots past the window's groups and padding are 0).
+//
+// Design (gfx950), HBM-bound: 0.5 byte per weight + 4 bytes per (row, group).
+// - Every wave-wide load is 1 KiB contiguous (16-byte lanes in order).
+// - v_mfma_f32_16x16x32_bf16: activations are the 16-row A operand (rows >= M
+//   are zero), 16 weight rows the B operand. Word w unpacks to bf16 128+q in
+//   K order with ((w >> 4i) & 0x000F000F) | 0x43004300: 0x4300 | q is the bf16
+//   bit pattern of 128+q, exact. Row sums XS = sum_k x come from the MFMA
+//   against ones, and sum_k x*(q-8) = C - 136*XS, so per group
+//     y += scale*C + (zero - 136*scale)*XS.
+// - A 512-thread block owns RT row tiles; its 8 waves take the 8 windows of a
+//   4096-wide K pass and keep that pass's activations in registers for all
+//   RT tiles. All loads of a pass are issued up front in the order they are
+//   consumed (raw buffer loads: masked rows/units read as zero); partial
+//   tiles of the 8 waves are summed through LDS.
 #include "w4_device.h"
 
 namespace w4 {
 
-constexpr int kDThreads = 256;
-constexpr int kDBatch = 8;          // units (64 K each) loaded per batch
+constexpr int kDThreads = 512;
+constexpr int kDWaves = kDThreads / kWave;
+constexpr int kWinK = 512;                 // K per window (8 units of 64)
+constexpr int kWTile = 4096;               // weight bytes per (row tile, window)
+constexpr int kSZTile = 16 * 8 * 2 * 2;    // scale/zero bytes per (row tile, window)
 
 __device__ __forceinline__ v8bf as_v8bf(v4i v) { return __builtin_bit_cast(v8bf, v); }
 
 __device__ __forceinline__ v4i unpack_bf16_128q(uint32_t w) {
-  // codes c0..c7 of the word (c_{2i} low nibble of byte i) -> bf16 128+c in
-  // element order [c0 c4 c1 c5 c2 c6 c3 c7]
   v4i r;
   r[0] = (int)((w & 0x000F000Fu) | 0x43004300u);
   r[1] = (int)(((w >> 4) & 0x000F000Fu) | 0x43004300u);
@@ -40,119 +54,207 @@ __device__ __forceinline__ v4i unpack_bf16_128q(uint32_t w) {
   return r;
 }
 
-__device__ __forceinline__ v4i permute_x(v4i raw) {
-  // raw = [x0x1, x2x3, x4x5, x6x7] (bf16 pairs) -> [x0x4, x1x5, x2x6, x3x7]
-  v4i r;
-  r[0] = (int)__builtin_amdgcn_perm((uint32_t)raw[2], (uint32_t)raw[0], 0x05040100u);
-  r[1] = (int)__builtin_amdgcn_perm((uint32_t)raw[2], (uint32_t)raw[0], 0x07060302u);
-  r[2] = (int)__builtin_amdgcn_perm((uint32_t)raw[3], (uint32_t)raw[1], 0x05040100u);
-  r[3] = (int)__builtin_amdgcn_perm((uint32_t)raw[3], (uint32_t)raw[1], 0x07060302u);
-  return r;
-}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__global__ __launch_bounds__(kDThreads) void w4a16_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero,
-    uint16_t* __restrict__ out, int M, int N, int K, int G, int upg) {
-  __shared__ float red[4][64][4];
+// RT: row tiles per block; UPG: 64-wide units per group (1, 2, 4 or 8)
+template <int RT, int UPG>
+__global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wt, const uint8_t* __restrict__ szt,
+    uint16_t* __restrict__ out, int M, int N, int K, int NT16, int KW) {
+  __shared__ __attribute__((aligned(16))) float red[kDWaves][RT][kWave][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 16;
   const int l16 = lane & 15, j = lane >> 4;
-  const int n = n0 + l16;                 // B column of this lane
-  const bool nval = n < N;
-  const bool mval = l16 < M;              // A row of this lane
-  const int64_t wrow = (int64_t)(nval ? n : 0) * (K >> 1);
-  const uint16_t* xrow = x + (int64_t)(mval ? l16 : 0) * K;
+  const int rt0 = blockIdx.x * RT;
+  const int U = K >> 6;
+  const uint32_t kOOB = 0x80000000u;         // past every buffer: loads return 0
 
-  // groups of this wave: g = wave, wave + 4, ...; units of a group are consecutive
-  const int ng = (G > wave) ? (G - wave + 3) / 4 : 0;
-  const int nu = ng * upg;                // units this wave processes
-  auto unit_of = [&](int idx) { return (wave + 4 * (idx / upg)) * upg + (idx % upg); };
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, (uint32_t)((int64_t)NT16 * KW * kWTile));
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(szt, (uint32_t)((int64_t)NT16 * KW * kSZTile));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
 
-  auto load_batch = [&](v2i (&wb)[kDBatch], int base) {
+  float y[RT][4];
 #pragma unroll
-    for (int i = 0; i < kDBatch; ++i) {
-      const int idx = base + i;
-      if (idx < nu && nval) {
-        const int u = unit_of(idx);
-        wb[i] = *reinterpret_cast<const v2i*>(w + wrow + u * 32 + 8 * j);
-      } else {
-        wb[i] = v2i{0, 0};
-      }
-    }
-  };
-
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[t][r] = 0.f;
   const v4i ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
-  v4f yacc = {0.f, 0.f, 0.f, 0.f};
-  v4f cacc = {0.f, 0.f, 0.f, 0.f}, xacc = {0.f, 0.f, 0.f, 0.f};
+  const v4f z4 = {0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](const v2i (&wb)[kDBatch], int base) {
+  for (int kw = wave; kw < KW; kw += kDWaves) {
+    // ---- all loads of this window, in consumption order
+    v4i xa[8][2];
+    const bool mv = l16 < M;
 #pragma unroll
-    for (int i = 0; i < kDBatch; ++i) {
-      const int idx = base + i;
-      if (idx >= nu) break;
-      const int u = unit_of(idx);
-      const int kb = u * 64 + 16 * j;
-      v4i xr0 = {0, 0, 0, 0}, xr1 = {0, 0, 0, 0};
-      if (mval) {
-        xr0 = *reinterpret_cast<const v4i*>(xrow + kb);
-        xr1 = *reinterpret_cast<const v4i*>(xrow + kb + 8);
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int u = kw * 8 + i;
+        xa[i][s] = buffer_load16(xr, (mv && u < U) ? (uint32_t)((l16 * K + u * 64 + 16 * j + 8 * s) * 2) : kOOB);
       }
-      const v8bf a0 = as_v8bf(permute_x(xr0)), a1 = as_v8bf(permute_x(xr1));
-      const v8bf b0 = as_v8bf(unpack_bf16_128q((uint32_t)wb[i][0]));
-      const v8bf b1 = as_v8bf(unpack_bf16_128q((uint32_t)wb[i][1]));
-      const bool first = (idx % upg) == 0;
-      const v4f z4 = {0.f, 0.f, 0.f, 0.f};
-      cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, first ? z4 : cacc, 0, 0, 0);
-      cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, cacc, 0, 0, 0);
-      xacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_v8bf(ones), first ? z4 : xacc, 0, 0, 0);
-      xacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_v8bf(ones), xacc, 0, 0, 0);
-      if ((idx % upg) == upg - 1) {
-        const int g = u / upg;
-        float s = 0.f, zp = 0.f;
-        if (nval) {
-          s = bf16_to_f32(scale[(int64_t)n * G + g]);
-          const float z = zero ? bf16_to_f32(zero[(int64_t)n * G + g]) : 0.f;
-          zp = fmaf(-136.f, s, z);
-        }
+    v4i wv[RT][4], szv[RT][2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yacc[r] = fmaf(s, cacc[r], fmaf(zp, xacc[r], yacc[r]));
+    for (int t = 0; t < RT; ++t) {
+      const int rt = rt0 + t;
+      const bool ok = rt < NT16;
+      const uint32_t wbase = (uint32_t)(((int64_t)rt * KW + kw) * kWTile) + 16u * lane;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) wv[t][p] = buffer_load16(wr, ok ? wbase + 1024u * p : kOOB);
+      const uint32_t sbase = (uint32_t)(((int64_t)rt * KW + kw) * kSZTile) + 32u * l16;
+      szv[t][0] = buffer_load16(sr, ok ? sbase : kOOB);
+      szv[t][1] = buffer_load16(sr, ok ? sbase + 16u : kOOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);       // keep the loads ahead of all compute
+
+    // ---- activation row sums per group (shared by the row tiles)
+    v4f xs[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const v4f c0 = (i % UPG == 0) ? z4 : xs[i > 0 ? i - 1 : 0];
+      const v4f a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]), as_v8bf(ones), c0, 0, 0, 0);
+      xs[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]), as_v8bf(ones), a, 0, 0, 0);
+    }
+
+    // ---- row tiles
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      v4f c = z4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w0 = (uint32_t)wv[t][i >> 1][(i & 1) * 2];
+        const uint32_t w1 = (uint32_t)wv[t][i >> 1][(i & 1) * 2 + 1];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]), as_v8bf(unpack_bf16_128q(w0)),
+                                                    (i % UPG == 0) ? z4 : c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]), as_v8bf(unpack_bf16_128q(w1)), c, 0, 0, 0);
+        if (i % UPG == UPG - 1) {
+          const int gi = i / UPG;                      // group slot 0..7
+          const uint32_t sz = (uint32_t)szv[t][gi >> 2][gi & 3];
+          const float s = bf16_lo(sz), z = bf16_hi(sz);
+          const float zp = fmaf(-136.f, s, z);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[t][r] = fmaf(s, c[r], fmaf(zp, xs[i][r], y[t][r]));
+        }
       }
     }
-  };
-
-  // two register batches: the next batch's loads are in flight while one computes
-  v2i wb0[kDBatch], wb1[kDBatch];
-  if (nu > 0) load_batch(wb0, 0);
-  for (int base = 0; base < nu; base += 2 * kDBatch) {
-    if (base + kDBatch < nu) load_batch(wb1, base + kDBatch);
-    process(wb0, base);
-    if (base + kDBatch >= nu) break;
-    if (base + 2 * kDBatch < nu) load_batch(wb0, base + 2 * kDBatch);
-    process(wb1, base + kDBatch);
   }
 
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][lane][r] = yacc[r];
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][t][lane][r] = y[t][r];
   __syncthreads();
-  {
-    const int m = tid >> 4, nn = tid & 15;     // output element (m, n0 + nn)
+  for (int e = tid; e < RT * 256; e += kDThreads) {
+    const int t = e >> 8, m = (e >> 4) & 15, nn = e & 15;   // output (m, 16*(rt0+t) + nn)
     const int l = nn + 16 * (m >> 2), r = m & 3;
-    const float y = red[0][l][r] + red[1][l][r] + red[2][l][r] + red[3][l][r];
-    if (m < M && n0 + nn < N) out[(int64_t)m * N + n0 + nn] = f32_to_bf16_rne(y);
+    float acc = 0.f;
+#pragma unroll
+    for (int w_ = 0; w_ < kDWaves; ++w_) acc += red[w_][t][l][r];
+    const int n = 16 * (rt0 + t) + nn;
+    if (m < M && n < N) out[(int64_t)m * N + n] = f32_to_bf16_rne(acc);
   }
 }
 
-hipError_t launch_w4a16(const void* x, const uint8_t* w, const void* scale, const void* zero,
-                        int64_t group, void* out, int64_t M, int64_t N, int64_t K,
-                        hipStream_t stream) {
+// ---------------------------------------------------------------- repack
+
+__device__ __forceinline__ uint32_t p5_code(const uint8_t* w, int N, int K, int n, int k) {
+  if (n >= N || k >= K) return 8u;
+  const uint8_t b = w[(int64_t)n * (K >> 1) + (k >> 1)];
+  return (k & 1) ? (uint32_t)(b >> 4) : (uint32_t)(b & 0xF);
+}
+
+// one thread per 32-bit word of the weight tiles
+__global__ __launch_bounds__(256) void w4a16_repack_w_kernel(const uint8_t* __restrict__ w, int N, int K, int KW,
+                                                             uint32_t* __restrict__ dst, int64_t words) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= words) return;
+  const int64_t tile = id / (kWTile / 4);
+  const int in = (int)(id % (kWTile / 4));
+  const int p = in >> 8, lane = (in >> 2) & 63, wi = in & 3;
+  const int rt = (int)(tile / KW), kw = (int)(tile % KW);
+  const int n = rt * 16 + (lane & 15), jj = lane >> 4;
+  const int u = kw * 8 + 2 * p + (wi >> 1);
+  const int kb = u * 64 + 16 * jj + 8 * (wi & 1);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = (i < 4) ? 2 * i : 2 * (i - 4) + 1;
+    word |= p5_code(w, N, K, n, kb + e) << (4 * i);
+  }
+  dst[id] = word;
+}
+
+// one thread per (row tile, window, row, slot): scale and zero of one group
+__global__ __launch_bounds__(256) void w4a16_repack_sz_kernel(const uint16_t* __restrict__ scale,
+                                                              const uint16_t* __restrict__ zero, int N, int G,
+                                                              int upg, int KW, uint32_t* __restrict__ dst,
+                                                              int64_t entries) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= entries) return;
+  const int slot = (int)(id & 7), row = (int)((id >> 3) & 15);
+  const int64_t tile = id >> 7;
+  const int rt = (int)(tile / KW), kw = (int)(tile % KW);
+  const int n = rt * 16 + row;
+  const int gpw = 8 / upg;
+  const int g = kw * gpw + slot;
+  uint32_t v = 0;
+  if (n < N && slot < gpw && g < G) {
+    const uint32_t s = scale[(int64_t)n * G + g];
+    const uint32_t z = zero ? zero[(int64_t)n * G + g] : 0u;
+    v = s | (z << 16);
+  }
+  dst[id] = v;
+}
+
+void w4a16_tiled_bytes(int64_t K, int64_t N, size_t* wbytes, size_t* szbytes) {
+  const int64_t NT16 = (N + 15) / 16, KW = (K + kWinK - 1) / kWinK;
+  *wbytes = (size_t)(NT16 * KW * kWTile);
+  *szbytes = (size_t)(NT16 * KW * kSZTile);
+}
+
+hipError_t launch_w4a16_repack(const uint8_t* w, const void* scale, const void* zero, int64_t group, int64_t K,
+                               int64_t N, void* w_tiled, void* sz_tiled, hipStream_t stream) {
+  const int NT16 = (int)((N + 15) / 16), KW = (int)((K + kWinK - 1) / kWinK);
+  const int64_t words = (int64_t)NT16 * KW * (kWTile / 4);
+  hipLaunchKernelGGL(w4a16_repack_w_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream, w, (int)N,
+                     (int)K, KW, static_cast<uint32_t*>(w_tiled), words);
+  const int64_t entries = (int64_t)NT16 * KW * 128;
+  hipLaunchKernelGGL(w4a16_repack_sz_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(scale), static_cast<const uint16_t*>(zero), (int)N,
+                     (int)(K / group), (int)(group / 64), KW, static_cast<uint32_t*>(sz_tiled), entries);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled, int64_t group, void* out,
+                        int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int G = (int)(K / group);
+  const int NT16 = (int)((N + 15) / 16), KW = (int)((K + kWinK - 1) / kWinK);
   const int upg = (int)(group / 64);
-  dim3 grid((unsigned)((N + 15) / 16)), block(kDThreads);
-  hipLaunchKernelGGL(w4a16_kernel, grid, block, 0, stream, static_cast<const uint16_t*>(x), w,
-                     static_cast<const uint16_t*>(scale), static_cast<const uint16_t*>(zero),
-                     static_cast<uint16_t*>(out), (int)M, (int)N, (int)K, G, upg);
+  // row tiles per block: enough blocks to cover ~all CUs, at most 4 tiles each
+  int rt = (NT16 + 255) / 256;
+  rt = rt < 1 ? 1 : (rt > 4 ? 4 : rt);
+  dim3 grid((unsigned)((NT16 + rt - 1) / rt)), block(kDThreads);
+  auto X = static_cast<const uint16_t*>(x);
+  auto Wt = static_cast<const uint8_t*>(w_tiled);
+  auto St = static_cast<const uint8_t*>(sz_tiled);
+  auto O = static_cast<uint16_t*>(out);
+  const int iM = (int)M, iN = (int)N, iK = (int)K;
+#define W4A16_LAUNCH(RT_, UPG_) \
+  hipLaunchKernelGGL((w4a16_kernel<RT_, UPG_>), grid, block, 0, stream, X, Wt, St, O, iM, iN, iK, NT16, KW)
+#define W4A16_RT(UPG_)                        \
+  switch (rt) {                               \
+    case 1: W4A16_LAUNCH(1, UPG_); break;     \
+    case 2: W4A16_LAUNCH(2, UPG_); break;     \
+    case 3: W4A16_LAUNCH(3, UPG_); break;     \
+    default: W4A16_LAUNCH(4, UPG_); break;    \
+  }
+  switch (upg) {
+    case 1: W4A16_RT(1) break;
+    case 2: W4A16_RT(2) break;
+    case 4: W4A16_RT(4) break;
+    default: W4A16_RT(8) break;
+  }
+#undef W4A16_RT
+#undef W4A16_LAUNCH
   return hipGetLastError();
 }
 

@@ -40,12 +40,15 @@ __device__ __forceinline__ int swz(int row, int kc) { return row * 128 + ((kc ^ 
 
 enum { kModeGroup = 0, kModeChannel = 1, kModePartials = 2 };
 
-template <int MODE, bool OUT_BF16>
+// GC: 64-deep chunks per weight group when known at compile time (1: group
+// 64, 2: group 128), 0: taken from group_chunks at run time.
+template <int MODE, bool OUT_BF16, int GC>
 __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
-    const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks,
+    const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
     int32_t* __restrict__ partials, int M, int N, int K, int KT, int tilesM, int tilesN) {
+  const int group_chunks = GC > 0 ? GC : group_chunks_rt;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
 
   // ---- tile of this block
@@ -112,9 +115,20 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   for (int j = 0; j < 4; ++j) ncol[j] = n0 + 64 * wn + 16 * j + (lane & 15);
   const int mrow0 = m0 + 64 * wm + 4 * (lane >> 4);   // + 16*i + r
 
-  auto load_scales = [&](int g, float (&sc)[4]) {
+  // Unconditional loads at clamped indices (no branch, no early wait); the
+  // value of a column past N is never stored.
+  int ncl[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j] = (ncol[j] < N) ? f16_to_f32(wscale[(int64_t)g * N + ncol[j]]) : 0.f;
+  for (int j = 0; j < 4; ++j) ncl[j] = min(ncol[j], N - 1);
+  auto load_scales_raw = [&](int g, uint16_t (&raw)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = wscale[(int64_t)g * N + ncl[j]];
+  };
+  auto load_scales = [&](int g, float (&sc)[4]) {
+    uint16_t raw[4];
+    load_scales_raw(g, raw);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[j] = f16_to_f32(raw[j]);
   };
 
   auto group_end = [&](int g, const float (&sc)[4]) {
@@ -162,21 +176,32 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     }
   };
 
-  // ---- main loop: two LDS stages, one barrier per K step
+  // ---- main loop: two LDS stages, one barrier per K step. The scales of the
+  // groups ending in K step tk+1 are fetched during step tk.
+  uint16_t scr[2][4];
+  auto fetch_step_scales = [&](int tk) {
+    if (MODE != kModeGroup) return;
+    const int cg0 = 2 * tk;
+    load_scales_raw(min(cg0 / group_chunks, G - 1), scr[0]);
+    load_scales_raw(min((cg0 + 1) / group_chunks, G - 1), scr[1]);
+  };
   gload(0);
+  fetch_step_scales(0);
   lstore(0);
   __syncthreads();
   for (int tk = 0; tk < KT; ++tk) {
     const int stage = tk & 1;
     const bool more = tk + 1 < KT;
-    if (more) gload(tk + 1);
     float sc[2][4];
-    const int cg0 = 2 * tk;
-    if (MODE == kModeGroup) {
-      // scales of the groups that end in this K step (chunks past K have none)
-      load_scales(cg0 / group_chunks, sc[0]);
-      if (cg0 + 1 < nchunks) load_scales((cg0 + 1) / group_chunks, sc[1]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[c][j] = f16_to_f32(scr[c][j]);
+    if (more) {
+      gload(tk + 1);
+      fetch_step_scales(tk + 1);
     }
+    const int cg0 = 2 * tk;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int cg = cg0 + c;
@@ -197,20 +222,26 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   }
 
   // ---- output: out = facc * a_scale / 16 + bias
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = OUT_BF16 ? bf16_to_f32(bias[ncl[j]]) : f16_to_f32(bias[ncl[j]]);
+  }
+  float sa[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sa[i][r] = a_scale[min(mrow0 + 16 * i + r, M - 1)] * 0.0625f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mrow0 + 16 * i + r;
-      if (m >= M) continue;
-      const float sa = a_scale[m] * 0.0625f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = ncol[j];
-        if (n >= N) continue;
-        float y = facc[i][j][r] * sa;
-        if (bias) y += OUT_BF16 ? bf16_to_f32(bias[n]) : f16_to_f32(bias[n]);
-        out[(int64_t)m * N + n] = OUT_BF16 ? f32_to_bf16_rne(y) : f32_to_f16_rne(y);
+        const float y = fmaf(facc[i][j][r], sa[i][r], bv[j]);
+        if (m < M && n < N) out[(int64_t)m * N + n] = OUT_BF16 ? f32_to_bf16_rne(y) : f32_to_f16_rne(y);
       }
     }
 }
@@ -223,31 +254,28 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
   const int KT = (int)((K + kBK - 1) / kBK);
   const int tilesM = (int)((M + kBM - 1) / kBM), tilesN = (int)((N + kBN - 1) / kBN);
   const int nchunks = (int)((K + 63) / 64);
-  const int group_chunks = (group == -1) ? nchunks : (int)(group / 64);
+  const int gc = (group == -1) ? nchunks : (int)(group / 64);
   dim3 grid((unsigned)(tilesM * tilesN)), block(kGThreads);
   auto W = static_cast<const v4i*>(w_tiled);
   auto S = static_cast<const uint16_t*>(w_scale);
   auto B = static_cast<const uint16_t*>(bias);
   auto O = static_cast<uint16_t*>(out);
   const int iM = (int)M, iN = (int)N, iK = (int)K;
+#define W4A8_LAUNCH(MODE_, BF16_, GC_)                                                                  \
+  hipLaunchKernelGGL((w4a8_gemm_kernel<MODE_, BF16_, GC_>), grid, block, 0, stream, a, a_scale, W, S, gc, B, O, \
+                     partials, iM, iN, iK, KT, tilesM, tilesN)
   if (partials) {
-    hipLaunchKernelGGL((w4a8_gemm_kernel<kModePartials, true>), grid, block, 0, stream, a, a_scale, W, S,
-                       group_chunks, B, O, partials, iM, iN, iK, KT, tilesM, tilesN);
+    W4A8_LAUNCH(kModePartials, true, 0);
   } else if (group == -1) {
-    if (out_bf16)
-      hipLaunchKernelGGL((w4a8_gemm_kernel<kModeChannel, true>), grid, block, 0, stream, a, a_scale, W, S,
-                         group_chunks, B, O, nullptr, iM, iN, iK, KT, tilesM, tilesN);
-    else
-      hipLaunchKernelGGL((w4a8_gemm_kernel<kModeChannel, false>), grid, block, 0, stream, a, a_scale, W, S,
-                         group_chunks, B, O, nullptr, iM, iN, iK, KT, tilesM, tilesN);
+    if (out_bf16) W4A8_LAUNCH(kModeChannel, true, 0); else W4A8_LAUNCH(kModeChannel, false, 0);
+  } else if (gc == 1) {
+    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 1); else W4A8_LAUNCH(kModeGroup, false, 1);
+  } else if (gc == 2) {
+    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 2); else W4A8_LAUNCH(kModeGroup, false, 2);
   } else {
-    if (out_bf16)
-      hipLaunchKernelGGL((w4a8_gemm_kernel<kModeGroup, true>), grid, block, 0, stream, a, a_scale, W, S,
-                         group_chunks, B, O, nullptr, iM, iN, iK, KT, tilesM, tilesN);
-    else
-      hipLaunchKernelGGL((w4a8_gemm_kernel<kModeGroup, false>), grid, block, 0, stream, a, a_scale, W, S,
-                         group_chunks, B, O, nullptr, iM, iN, iK, KT, tilesM, tilesN);
+    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 0); else W4A8_LAUNCH(kModeGroup, false, 0);
   }
+#undef W4A8_LAUNCH
   return hipGetLastError();
 }
 

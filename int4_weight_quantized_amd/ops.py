@@ -27,7 +27,9 @@ _SIGS = {
     "w4_repack": [_P, _I, _I64, _I64, _I64, _P, _P],
     "w4a8_gemm": [_P, _P, _P, _P, _I, _I64, _P, _P, _I, _I64, _I64, _I64, _P],
     "w4a8_gemm_partials": [_P, _P, _I64, _P, _I64, _I64, _I64, _P],
-    "w4a16_gemm": [_P, _P, _P, _P, _I, _I64, _P, _I64, _I64, _I64, _P],
+    "w4a16_repack_bytes": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)],
+    "w4a16_repack": [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _P],
+    "w4a16_gemm": [_P, _P, _P, _I64, _P, _I64, _I64, _I64, _P],
     "w4a8_grouped_gemm": [_P, _I, _P, _P, _P, _P, _I64, _P, _P, _I, _I64, _P, _I, _I64, _I64, _I64, _I64, _P],
     "w4_last_error": [],
     "w4_version": [],
@@ -145,14 +147,31 @@ def w4a8_gemm_partials(a, w_tiled, group: int, N: int, stream=None):
     return P
 
 
-def w4a16_gemm(x, w, scale, zero, group: int, out=None, stream=None):
+def w4a16_repack_bytes(K: int, N: int, group: int):
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("w4a16_repack_bytes", lib().w4a16_repack_bytes(K, N, group, ctypes.byref(wb), ctypes.byref(sb)))
+    return wb.value, sb.value
+
+
+def w4a16_repack(w, scale, zero, group: int, stream=None):
+    """Load-time repack of byte-layout weights [N, K/2] with bf16 scale/zero [N, K/group]
+    into (w_tiled, sz_tiled) uint8 buffers."""
+    N, K = w.shape[0], w.shape[1] * 2
+    wb, sb = w4a16_repack_bytes(K, N, group)
+    wt = torch.empty((wb,), dtype=torch.uint8, device=w.device)
+    st = torch.empty((sb,), dtype=torch.uint8, device=w.device)
+    _check("w4a16_repack", lib().w4a16_repack(
+        _ptr(w), _ptr(scale), _ptr(zero), _half_code(scale.dtype), group, K, N, _ptr(wt), _ptr(st),
+        _stream(stream)))
+    return wt, st
+
+
+def w4a16_gemm(x, w_tiled, sz_tiled, group: int, N: int, out=None, stream=None):
     M, K = x.shape
-    N = w.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _check("w4a16_gemm", lib().w4a16_gemm(
-        _ptr(x), _ptr(w), _ptr(scale), _ptr(zero), _half_code(scale.dtype), group, _ptr(out),
-        M, N, K, _stream(stream)))
+        _ptr(x), _ptr(w_tiled), _ptr(sz_tiled), group, _ptr(out), M, N, K, _stream(stream)))
     return out
 
 

@@ -233,7 +233,8 @@ def _w4a16_run(d, with_zero=True):
     w = torch.from_numpy(d["w"]).to(DEV)
     s = dev_half(d["scale"], "bf16")
     z = dev_half(d["zero"], "bf16") if with_zero else None
-    return ops.w4a16_gemm(x, w, s, z, d["group"])
+    wt, st = ops.w4a16_repack(w, s, z, d["group"])
+    return ops.w4a16_gemm(x, wt, st, d["group"], d["N"])
 
 
 @pytest.mark.parametrize("M", [1, 8])
@@ -247,7 +248,7 @@ def test_w4a16_decode_workload(M):
 
 @pytest.mark.parametrize("M,K,N,group,zero", [
     (16, 64, 8, 64, True), (3, 192, 24, 64, True), (2, 512, 136, 128, True), (1, 256, 40, 256, False),
-    (13, 14336, 64, 64, True), (8, 4096, 1000, 64, True)])
+    (13, 14336, 64, 64, True), (8, 4096, 1000, 64, True), (4, 1536, 72, 512, True), (5, 8192, 4104, 128, True)])
 def test_w4a16_edges(M, K, N, group, zero):
     d = W.w4a16_inputs(M, K, N, group, seed=M + K + N)
     y = _w4a16_run(d, with_zero=zero)

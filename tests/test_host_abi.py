@@ -28,7 +28,7 @@ def L():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for must in ("w4a8_quantize_act", "w4a8_gemm", "w4a16_gemm", "w4a8_grouped_gemm", "w4_repack",
+    for must in ("w4a8_quantize_act", "w4a8_gemm", "w4a16_gemm", "w4a16_repack", "w4a8_grouped_gemm", "w4_repack",
                  "w4_repack_bytes", "w4a8_gemm_partials", "w4_last_error", "w4_version"):
         assert must in names
 
@@ -60,7 +60,8 @@ def test_scale_dtype_rule(L):
 def test_group_rules(L):
     assert L.w4a8_gemm(None, None, None, None, 2, 96, None, None, 1, 16, 256, 288, None) == -3
     assert L.w4a8_gemm(None, None, None, None, 2, 128, None, None, 1, 16, 256, 192, None) == -3
-    assert L.w4a16_gemm(None, None, None, None, 1, 48, None, 1, 256, 256, None) == -3
+    assert L.w4a16_gemm(None, None, None, 48, None, 1, 256, 256, None) == -3
+    assert L.w4a16_gemm(None, None, None, 1024, None, 1, 256, 2048, None) == -3
     assert L.w4a8_grouped_gemm(None, 5, None, None, None, None, 4, None, None, 2, 64, None, 1,
                                8, 8, 256, 256, None) == -3
 
@@ -75,11 +76,19 @@ def test_empty_inputs_are_noops(L):
     # M == 0 (or N == 0) enqueues nothing and succeeds even with null buffers
     assert L.w4a8_gemm(None, None, None, None, 2, 128, None, None, 1, 0, 256, 256, None) == 0
     assert L.w4a8_quantize_act(None, 1, 0, 256, 256, None, 4, None, None, 0, None) == 0
-    assert L.w4a16_gemm(None, None, None, None, 1, 64, None, 0, 256, 256, None) == 0
+    assert L.w4a16_gemm(None, None, None, 64, None, 0, 256, 256, None) == 0
 
 
 def test_decode_batch_limit(L):
-    assert L.w4a16_gemm(None, None, None, None, 1, 64, None, 17, 256, 256, None) == -5
+    assert L.w4a16_gemm(None, None, None, 64, None, 17, 256, 256, None) == -5
+
+
+def test_w4a16_repack_bytes(L):
+    wb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.w4a16_repack_bytes(4096, 14336, 64, ctypes.byref(wb), ctypes.byref(sb)) == 0
+    assert wb.value == 14336 * 4096 // 2 and sb.value == 14336 * 64 * 4
+    assert L.w4a16_repack_bytes(192, 24, 64, ctypes.byref(wb), ctypes.byref(sb)) == 0
+    assert wb.value == 2 * 1 * 4096 and sb.value == 2 * 1 * 512      # 16-row tiles x 512-wide windows
 
 
 def test_repack_bytes(L):
