@@ -24,10 +24,11 @@
 // - Every wave-wide load is 1 KiB contiguous (16-byte lanes in order).
 // - v_mfma_f32_16x16x32_bf16: activations are the 16-row A operand (rows >= M
 //   are zero), 16 weight rows the B operand. Word w unpacks to bf16 128+q in
-//   K order with ((w >> 4i) & 0x000F000F) | 0x43004300: 0x4300 | q is the bf16
-//   bit pattern of 128+q, exact. Row sums XS = sum_k x come from the MFMA
-//   against ones, and sum_k x*(q-8) = C - 136*XS, so per group
-//     y += scale*C + (zero - 136*scale)*XS.
+//   K order with ((w >> 4i) & 0x000F000F) | 0x43004300 (one v_and_or_b32):
+//   0x4300 | q is the bf16 bit pattern of 128+q, exact. Row sums XS = sum_k x
+//   come from the MFMA against ones; the group's product accumulator starts
+//   at -136*XS, so it ends at sum_k x*(q-8), and per group
+//     y += scale*C + zero*XS.
 // - A 512-thread block owns RT row tiles; its 8 waves take the 8 windows of a
 //   4096-wide K pass and keep that pass's activations in registers for all
 //   RT tiles. All loads of a pass are issued up front in the order they are
@@ -45,12 +46,21 @@ constexpr int kSZTile = 16 * 8 * 2 * 2;    // scale/zero bytes per (row tile, wi
 
 __device__ __forceinline__ v8bf as_v8bf(v4i v) { return __builtin_bit_cast(v8bf, v); }
 
-__device__ __forceinline__ v4i unpack_bf16_128q(uint32_t w) {
+// (a & mask) | magic in one v_and_or_b32. gfx9 VOP3 encodes no literal and
+// reads at most one scalar operand, so the caller keeps the mask in an SGPR
+// and the magic in a VGPR, both made opaque so the compiler cannot fold them
+// back into literals; the and-or itself stays plain code.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask_s, uint32_t magic_v) {
+  return (a & mask_s) | magic_v;
+}
+
+// word -> 4 registers of bf16 pairs 128+q, K order (see the tiled layout)
+__device__ __forceinline__ v4i unpack_bf16_128q(uint32_t w, uint32_t mask_s, uint32_t magic_v) {
   v4i r;
-  r[0] = (int)((w & 0x000F000Fu) | 0x43004300u);
-  r[1] = (int)(((w >> 4) & 0x000F000Fu) | 0x43004300u);
-  r[2] = (int)(((w >> 8) & 0x000F000Fu) | 0x43004300u);
-  r[3] = (int)(((w >> 12) & 0x000F000Fu) | 0x43004300u);
+  r[0] = (int)and_or(w, mask_s, magic_v);
+  r[1] = (int)and_or(w >> 4, mask_s, magic_v);
+  r[2] = (int)and_or(w >> 8, mask_s, magic_v);
+  r[3] = (int)and_or(w >> 12, mask_s, magic_v);
   return r;
 }
 
@@ -80,6 +90,9 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
     for (int r = 0; r < 4; ++r) y[t][r] = 0.f;
   const v4i ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
   const v4f z4 = {0.f, 0.f, 0.f, 0.f};
+  uint32_t mask_s, magic_v;
+  asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(mask_s));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic_v));
 
   for (int kw = wave; kw < KW; kw += kDWaves) {
     // ---- all loads of this window, in consumption order
@@ -106,13 +119,22 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);       // keep the loads ahead of all compute
 
-    // ---- activation row sums per group (shared by the row tiles)
-    v4f xs[8];
+    // ---- activation row sums per group (shared by the row tiles): XS of
+    // group gi in xs[gi]; the group's product accumulator starts at -136*XS
+    v4f xs[8], xinit[8];
+    {
+      v4f run = z4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const v4f c0 = (i % UPG == 0) ? z4 : xs[i > 0 ? i - 1 : 0];
-      const v4f a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]), as_v8bf(ones), c0, 0, 0, 0);
-      xs[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]), as_v8bf(ones), a, 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const v4f a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]), as_v8bf(ones),
+                                                              (i % UPG == 0) ? z4 : run, 0, 0, 0);
+        run = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]), as_v8bf(ones), a, 0, 0, 0);
+        if (i % UPG == UPG - 1) {
+          xs[i / UPG] = run;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xinit[i / UPG][r] = -136.f * run[r];
+        }
+      }
     }
 
     // ---- row tiles
@@ -123,16 +145,18 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
       for (int i = 0; i < 8; ++i) {
         const uint32_t w0 = (uint32_t)wv[t][i >> 1][(i & 1) * 2];
         const uint32_t w1 = (uint32_t)wv[t][i >> 1][(i & 1) * 2 + 1];
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]), as_v8bf(unpack_bf16_128q(w0)),
-                                                    (i % UPG == 0) ? z4 : c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]), as_v8bf(unpack_bf16_128q(w1)), c, 0, 0, 0);
+        // c = sum_k x*(128+q) - 136*XS = sum_k x*(q-8) over the group
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]),
+                                                    as_v8bf(unpack_bf16_128q(w0, mask_s, magic_v)),
+                                                    (i % UPG == 0) ? xinit[i / UPG] : c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]),
+                                                    as_v8bf(unpack_bf16_128q(w1, mask_s, magic_v)), c, 0, 0, 0);
         if (i % UPG == UPG - 1) {
           const int gi = i / UPG;                      // group slot 0..7
           const uint32_t sz = (uint32_t)szv[t][gi >> 2][gi & 3];
           const float s = bf16_lo(sz), z = bf16_hi(sz);
-          const float zp = fmaf(-136.f, s, z);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) y[t][r] = fmaf(s, c[r], fmaf(zp, xs[i][r], y[t][r]));
+          for (int r = 0; r < 4; ++r) y[t][r] = fmaf(s, c[r], fmaf(z, xs[gi][r], y[t][r]));
         }
       }
     }
