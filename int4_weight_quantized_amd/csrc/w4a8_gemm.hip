@@ -9,36 +9,45 @@
 //   out[m,n] = a_scale[m] * sum_g w_scale[g,n] * P[m,g,n] + bias[n]
 //
 // Design (gfx950):
-// - 256 threads, block tile 128x128, four waves of 64x64, K step 128,
-//   two LDS stages (64 KiB) so two blocks share a CU.
-// - A (int8 codes) streams global -> LDS with 16-byte raw buffer loads
-//   whose range check zero-fills rows past M and bytes past the matrix.
-// - B is read from the tiled int4 layout (8 KiB contiguous per tile, fully
-//   coalesced) and unpacked once per block into LDS as int8 bytes equal to
-//   16*(q-8): the stored nibble is q^8, so a mask (and a 4-bit shift) is the
-//   whole unpack. The MFMA therefore accumulates 16*P; the factor 1/16 is
-//   folded into the final per-row scale (exact: a power of two).
-// - LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled by (row & 7) so
-//   both the tile writes and the MFMA fragment reads are conflict-free.
-// - v_mfma_i32_16x16x64_i8: each wave issues 16 MFMAs per 64-deep chunk. At
-//   a K-group boundary the int32 sums are converted and FMA'd into fp32
-//   accumulators with the group's fp16 scale; the next chunk restarts the
-//   int32 sums with C = 0.
+// - 256 threads, block tile 128x128, four waves of 64x64, K step 128, two
+//   LDS stages (68 KiB) so two blocks share a CU and their waves interleave
+//   on each SIMD.
+// - Loads are raw buffer loads issued one K step ahead of use. A (int8
+//   codes) goes straight from memory to LDS, its range check zero-filling
+//   rows past M; B (the tiled int4 layout, 8 KiB contiguous per tile) comes
+//   through registers.
+// - B is unpacked once per block into LDS as int8 bytes 16*(q-8): the stored
+//   nibble is q^8, so a mask (and a 4-bit shift) is the whole unpack. The
+//   MFMA accumulates 16*P; 1/16 is folded into the row scale (exact).
+// - A rows in LDS are 128 bytes with XOR-swizzled 16-byte chunks, B rows are
+//   padded to 144 bytes: fragment reads and tile writes are bank-conflict
+//   free, and every fragment address is a base register plus an immediate.
+// - v_mfma_i32_16x16x64_i8. With one group per K step (group 128) a wave's
+//   64x64 tile is worked in two 32-row halves: while one half's MFMAs run,
+//   the other half's finished group goes through its epilogue (int32 ->
+//   fp32, FMA with the group's fp16 scale), so the vector ALU work overlaps
+//   the matrix core. Other group sizes apply the epilogue after each group.
 // - Tiles are visited in groups of 8 tile-rows, and block ids are remapped
 //   so each XCD (own L2) works on a contiguous range of tiles.
+#include <type_traits>
+
 #include "w4_device.h"
 
 namespace w4 {
 
 constexpr int kBM = 128, kBN = 128, kBK = 128;
 constexpr int kGThreads = 256;
-constexpr int kStageA = kBM * kBK;               // bytes
-constexpr int kStageB = kBN * kBK;
+constexpr int kRow = 144;                          // padded LDS row, bytes
+constexpr int kStageA = kBM * kBK;                 // A rows unpadded, chunks swizzled
+constexpr int kStageB = kBN * kRow;                // B rows padded
 constexpr int kStage = kStageA + kStageB;
 
-__device__ __forceinline__ int swz(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
-
 enum { kModeGroup = 0, kModeChannel = 1, kModePartials = 2 };
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // GC: 64-deep chunks per weight group when known at compile time (1: group
 // 64, 2: group 128), 0: taken from group_chunks at run time.
@@ -48,8 +57,9 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
     int32_t* __restrict__ partials, int M, int N, int K, int KT, int tilesM, int tilesN) {
-  const int group_chunks = GC > 0 ? GC : group_chunks_rt;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  const int group_chunks = GC > 0 ? GC : group_chunks_rt;
+  constexpr bool kPingPong = (MODE == kModeGroup && GC == 2);
 
   // ---- tile of this block
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -66,39 +76,60 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   const int nchunks = (K + 63) >> 6;
   const int G = (MODE == kModeChannel) ? 1 : nchunks / group_chunks;
 
-  // ---- global -> register staging
+  // ---- global loads: fixed per-lane offsets, K step in the scalar offset.
+  // A goes straight to LDS (buffer load with the LDS destination): wave w's
+  // load i fills stage rows 32w + 8i .. +7, one KiB, lane L landing at row
+  // 32w + 8i + L/8, physical 16-byte chunk L%8. The lane fetches the logical
+  // chunk that belongs there under the swizzle p = kc ^ f(row), with
+  // f(row) = (row & 7) ^ ((row >> 3) & 1): 16 consecutive rows read at one
+  // logical chunk then hit distinct banks. Bit 3 of the row is i & 1, so two
+  // per-lane offsets serve all four loads.
   const int rows_valid = min(kBM, M - m0);
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A + (int64_t)m0 * K, (uint32_t)rows_valid * (uint32_t)K);
-  const int arow0 = tid >> 3, akc = tid & 7;
-  v4i pa[4], pb[2];
-  auto gload = [&](int tk) {
-    const uint32_t k0 = (uint32_t)tk * kBK + 16u * akc;
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      make_rsrc(reinterpret_cast<const uint8_t*>(Wt) + (int64_t)tn * KT * kTileBytes, (uint32_t)KT * kTileBytes);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  uint32_t a_voff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pa[i] = buffer_load16(arsrc, (uint32_t)(arow0 + 32 * i) * (uint32_t)K + k0);
-    const v4i* wt = Wt + (((int64_t)tn * KT + tk) << 9);
-    pb[0] = wt[tid];
-    pb[1] = wt[tid + kGThreads];
+  for (int par = 0; par < 2; ++par)
+    a_voff[par] = (uint32_t)(32 * wave + lrow) * (uint32_t)K + 16u * (uint32_t)(lchunk ^ lrow ^ par);
+  const uint32_t w_voff = 16u * tid;                                               // units tid, tid+256
+  v4i pb[2];
+  auto gload = [&](int tk, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    const uint32_t ks = (uint32_t)tk * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)   // whole offset in the range-checked VGPR operand
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kStage + (32 * wave_u + 8 * i) * kBK), 16,
+          a_voff[i & 1] + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
+    const uint32_t ws = (uint32_t)tk * kTileBytes;
+    pb[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws, 0);
+    pb[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws + 4096u, 0);
   };
-  auto lstore = [&](int stage) {
-    uint8_t* la = lds + stage * kStage;
-    uint8_t* lb = la + kStageA;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i*>(la + swz(arow0 + 32 * i, akc)) = pa[i];
+  // B unit u (row u/4, K quarter u%4): its low nibbles unpack to K
+  // 32(u%4)+0..15, its high nibbles to +16..31 (padded rows).
+  const int b_wo = (tid >> 2) * kRow + 32 * (tid & 3);
+  auto lstore_b = [&](auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    uint8_t* lb = lds + ST * kStage + kStageA;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int u = tid + kGThreads * i, nl = u >> 2, kq = u & 3;
       v4i lo, hi;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         lo[c] = (int)(((uint32_t)pb[i][c] << 4) & 0xF0F0F0F0u);
         hi[c] = (int)((uint32_t)pb[i][c] & 0xF0F0F0F0u);
       }
-      *reinterpret_cast<v4i*>(lb + swz(nl, 2 * kq)) = lo;
-      *reinterpret_cast<v4i*>(lb + swz(nl, 2 * kq + 1)) = hi;
+      *reinterpret_cast<v4i*>(lb + b_wo + 64 * kRow * i) = lo;
+      *reinterpret_cast<v4i*>(lb + b_wo + 64 * kRow * i + 16) = hi;
     }
   };
+  // the step's A tile (LDS DMA) and B words must have landed before the barrier
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
-  // ---- accumulators
+  // ---- accumulators: acc[i][j] int32 16x16 sub-tiles, facc fp32
   v4i acc[4][4];
   float facc[4][4][4];
 #pragma unroll
@@ -115,26 +146,26 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   for (int j = 0; j < 4; ++j) ncol[j] = n0 + 64 * wn + 16 * j + (lane & 15);
   const int mrow0 = m0 + 64 * wm + 4 * (lane >> 4);   // + 16*i + r
 
-  // Unconditional loads at clamped indices (no branch, no early wait); the
-  // value of a column past N is never stored.
-  int ncl[4];
+  // fp16 scales of group g for the lane's 4 columns, two per register, at
+  // clamped columns: a column past N is never stored
+  const __amdgpu_buffer_rsrc_t srsrc =
+      make_rsrc(wscale, (MODE == kModePartials) ? 0u : (uint32_t)((int64_t)G * N * 2));
+  uint32_t s_voff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ncl[j] = min(ncol[j], N - 1);
-  auto load_scales_raw = [&](int g, uint16_t (&raw)[4]) {
+  for (int j = 0; j < 4; ++j) s_voff[j] = 2u * (uint32_t)min(ncol[j], N - 1);
+  auto fetch_scales = [&](int g, h2 (&raw)[2]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) raw[j] = wscale[(int64_t)g * N + ncl[j]];
-  };
-  auto load_scales = [&](int g, float (&sc)[4]) {
-    uint16_t raw[4];
-    load_scales_raw(g, raw);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j] = f16_to_f32(raw[j]);
+    for (int j = 0; j < 4; ++j)
+      raw[j >> 1][j & 1] = __builtin_bit_cast(
+          _Float16, __builtin_amdgcn_raw_buffer_load_b16(srsrc, s_voff[j], (uint32_t)g * (uint32_t)N * 2u, 0));
   };
 
-  auto group_end = [&](int g, const float (&sc)[4]) {
-    if (MODE == kModePartials) {
+  // group epilogue for sub-tile rows [I0, I1)
+  auto epilogue = [&](auto I0c, auto I1c, const h2 (&raw)[2], int g) {
+    constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
+    if constexpr (MODE == kModePartials) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = I0; i < I1; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = mrow0 + 16 * i + r;
@@ -145,87 +176,170 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
         }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = I0; i < I1; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+          const float sc = (float)raw[j >> 1][j & 1];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) facc[i][j][r] = fmaf((float)acc[i][j][r], sc[j], facc[i][j][r]);
+          for (int r = 0; r < 4; ++r) facc[i][j][r] = fmaf((float)acc[i][j][r], sc, facc[i][j][r]);
+        }
     }
   };
 
-  auto compute_chunk = [&](int stage, int c, bool fresh) {
-    const uint8_t* la = lds + stage * kStage;
-    const uint8_t* lb = la + kStageA;
-    const int kc = 4 * c + (lane >> 4);
-    v4i af[4], bf[4];
+  // fragment reads: lane row (lane & 15), 16-byte chunk (lane >> 4); +64
+  // bytes per 64-deep chunk and +16 rows per sub-tile are immediates
+  const int fl = (lane & 7) ^ ((lane >> 3) & 1);          // f(row) of the lane's fragment rows
+  int a_ro[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i*>(la + swz(64 * wm + 16 * i + (lane & 15), kc));
+  for (int c = 0; c < 2; ++c) a_ro[c] = (64 * wm + (lane & 15)) * kBK + 16 * ((4 * c + (lane >> 4)) ^ fl);
+  const int b_ro = (64 * wn + (lane & 15)) * kRow + 16 * (lane >> 4);
+  auto read_b = [&](auto STc, int c, v4i (&bf)[4]) {
+    constexpr int ST = decltype(STc)::value;
+    const uint8_t* lb = lds + ST * kStage + kStageA + b_ro + 64 * c;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const v4i*>(lb + swz(64 * wn + 16 * j + (lane & 15), kc));
-    if (fresh) {
-      const v4i z = {0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const v4i*>(lb + 16 * kRow * j);
+  };
+  auto mfma_rows = [&](auto STc, int c, auto I0c, auto I1c, bool fresh, const v4i (&bf)[4]) {
+    constexpr int ST = decltype(STc)::value;
+    constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
+    const uint8_t* la = lds + ST * kStage + a_ro[c];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = I0; i < I1; ++i) {
+      const v4i af = *reinterpret_cast<const v4i*>(la + 16 * kBK * i);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], z, 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[j], fresh ? v4i{0, 0, 0, 0} : acc[i][j], 0, 0, 0);
     }
   };
 
-  // ---- main loop: two LDS stages, one barrier per K step. The scales of the
-  // groups ending in K step tk+1 are fetched during step tk.
-  uint16_t scr[2][4];
-  auto fetch_step_scales = [&](int tk) {
-    if (MODE != kModeGroup) return;
-    const int cg0 = 2 * tk;
-    load_scales_raw(min(cg0 / group_chunks, G - 1), scr[0]);
-    load_scales_raw(min((cg0 + 1) / group_chunks, G - 1), scr[1]);
+  auto read_a = [&](auto STc, int i, int c) -> v4i {
+    constexpr int ST = decltype(STc)::value;
+    return *reinterpret_cast<const v4i*>(lds + ST * kStage + a_ro[c] + 16 * kBK * i);
   };
-  gload(0);
-  fetch_step_scales(0);
-  lstore(0);
+  auto mfma_row = [&](int i, const v4i& af, const v4i (&bf)[4], bool fresh) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[j], fresh ? v4i{0, 0, 0, 0} : acc[i][j], 0, 0, 0);
+  };
+  auto interleave8 = [&]() {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+  };
+
+  // ---- prologue: tile 0 to LDS stage 0
+  gload(0, IC<0>{});
+  h2 scr_cur[2] = {h2{0, 0}, h2{0, 0}}, scr_prev[2] = {h2{0, 0}, h2{0, 0}};
+  if constexpr (kPingPong) fetch_scales(0, scr_cur);
+  lstore_b(IC<0>{});
+  wait_loads();
   __syncthreads();
-  for (int tk = 0; tk < KT; ++tk) {
-    const int stage = tk & 1;
-    const bool more = tk + 1 < KT;
-    float sc[2][4];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc[c][j] = f16_to_f32(scr[c][j]);
-    if (more) {
-      gload(tk + 1);
-      fetch_step_scales(tk + 1);
-    }
-    const int cg0 = 2 * tk;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int cg = cg0 + c;
-      if (cg >= nchunks) break;
-      const bool fresh = (MODE == kModeChannel) ? (cg == 0) : (cg % group_chunks == 0);
-      compute_chunk(stage, c, fresh);
-      if (MODE != kModeChannel && (cg + 1) % group_chunks == 0) group_end(cg / group_chunks, sc[c]);
-    }
-    if (more) lstore(stage ^ 1);
-    __syncthreads();
-  }
-  if (MODE == kModePartials) return;
 
-  if (MODE == kModeChannel) {
-    float sc[4];
-    load_scales(0, sc);
-    group_end(0, sc);
+  // K step tk reads LDS stage ST = tk & 1 while tile tk + 1 streams into the
+  // other stage (A directly, B through registers at the end of the step).
+  // Past the last tile the load repeats it, which keeps the body branch-free.
+  auto kstep = [&](int tk, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    gload(min(tk + 1, KT - 1), IC<ST ^ 1>{});
+    if constexpr (kPingPong) {
+      // Four quarters, each eight MFMAs with four vector ALU ops after each:
+      //   Q1  rows 0-1, chunk 0 (fresh)  |  rows 2-3 finish group tk - 1 (row 2)
+      //   Q2  rows 0-1, chunk 1          |  (row 3)
+      //   Q3  rows 2-3, chunk 0 (fresh)  |  rows 0-1 finish group tk (row 0)
+      //   Q4  rows 2-3, chunk 1          |  (row 1), then B unpack and store
+      // At tk = 0 rows 2-3 are still zero, so their epilogue adds nothing.
+      h2 scr_next[2];
+      fetch_scales(min(tk + 1, G - 1), scr_next);
+      v4i b0[4], b1[4];
+      read_b(IC<ST>{}, 0, b0);
+      read_b(IC<ST>{}, 1, b1);
+      const v4i a00 = read_a(IC<ST>{}, 0, 0), a10 = read_a(IC<ST>{}, 1, 0);
+      const v4i a01 = read_a(IC<ST>{}, 0, 1), a11 = read_a(IC<ST>{}, 1, 1);
+      mfma_row(0, a00, b0, true);
+      mfma_row(1, a10, b0, true);
+      epilogue(IC<2>{}, IC<3>{}, scr_prev, tk - 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 10, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      interleave8();
+      __builtin_amdgcn_sched_barrier(0);
+
+      const v4i a20 = read_a(IC<ST>{}, 2, 0), a30 = read_a(IC<ST>{}, 3, 0);
+      mfma_row(0, a01, b1, false);
+      mfma_row(1, a11, b1, false);
+      epilogue(IC<3>{}, IC<4>{}, scr_prev, tk - 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      interleave8();
+      __builtin_amdgcn_sched_barrier(0);
+
+      const v4i a21 = read_a(IC<ST>{}, 2, 1), a31 = read_a(IC<ST>{}, 3, 1);
+      mfma_row(2, a20, b0, true);
+      mfma_row(3, a30, b0, true);
+      epilogue(IC<0>{}, IC<1>{}, scr_cur, tk);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      interleave8();
+      __builtin_amdgcn_sched_barrier(0);
+
+      mfma_row(2, a21, b1, false);
+      mfma_row(3, a31, b1, false);
+      epilogue(IC<1>{}, IC<2>{}, scr_cur, tk);
+      lstore_b(IC<ST ^ 1>{});
+      interleave8();
+      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        scr_prev[j] = scr_cur[j];
+        scr_cur[j] = scr_next[j];
+      }
+    } else {
+      // scales of the groups ending in this step (at most two)
+      h2 s0[2], s1[2];
+      const int cg0 = 2 * tk;
+      if constexpr (MODE == kModeGroup) {
+        fetch_scales(min(cg0 / group_chunks, G - 1), s0);
+        fetch_scales(min((cg0 + 1) / group_chunks, G - 1), s1);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int cg = cg0 + c;
+        if (cg >= nchunks) break;
+        const bool fresh = (MODE == kModeChannel) ? (cg == 0) : (cg % group_chunks == 0);
+        v4i bf[4];
+        read_b(IC<ST>{}, c, bf);
+        mfma_rows(IC<ST>{}, c, IC<0>{}, IC<4>{}, fresh, bf);
+        if (MODE != kModeChannel && (cg + 1) % group_chunks == 0) epilogue(IC<0>{}, IC<4>{}, c ? s1 : s0, cg / group_chunks);
+      }
+      lstore_b(IC<ST ^ 1>{});
+    }
+    wait_loads();
+    __syncthreads();
+  };
+
+  int tk = 0;
+  for (; tk + 1 < KT; tk += 2) {
+    kstep(tk, IC<0>{});
+    kstep(tk + 1, IC<1>{});
+  }
+  if (tk < KT) kstep(tk, IC<0>{});
+  if constexpr (kPingPong) epilogue(IC<2>{}, IC<4>{}, scr_prev, KT - 1);
+  if constexpr (MODE == kModePartials) return;
+
+  if constexpr (MODE == kModeChannel) {
+    h2 raw[2];
+    fetch_scales(0, raw);
+    epilogue(IC<0>{}, IC<4>{}, raw, 0);
   }
 
   // ---- output: out = facc * a_scale / 16 + bias
   float bv[4] = {0.f, 0.f, 0.f, 0.f};
   if (bias) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = OUT_BF16 ? bf16_to_f32(bias[ncl[j]]) : f16_to_f32(bias[ncl[j]]);
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t b = bias[min(ncol[j], N - 1)];
+      bv[j] = OUT_BF16 ? bf16_to_f32(b) : f16_to_f32(b);
+    }
   }
   float sa[4][4];
 #pragma unroll
