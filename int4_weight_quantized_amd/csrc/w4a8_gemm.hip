@@ -10,7 +10,7 @@
 //
 // Design (gfx950):
 // - 256 threads, block tile 128x128, four waves of 64x64, K step 128, two
-//   LDS stages (68 KiB) so two blocks share a CU and their waves interleave
+//   LDS stages (64 KiB) so two blocks share a CU and their waves interleave
 //   on each SIMD.
 // - Loads are raw buffer loads issued one K step ahead of use. A (int8
 //   codes) goes straight from memory to LDS, its range check zero-filling
@@ -19,9 +19,10 @@
 // - B is unpacked once per block into LDS as int8 bytes 16*(q-8): the stored
 //   nibble is q^8, so a mask (and a 4-bit shift) is the whole unpack. The
 //   MFMA accumulates 16*P; 1/16 is folded into the row scale (exact).
-// - A rows in LDS are 128 bytes with XOR-swizzled 16-byte chunks, B rows are
-//   padded to 144 bytes: fragment reads and tile writes are bank-conflict
-//   free, and every fragment address is a base register plus an immediate.
+// - A and B rows in LDS are 128 bytes; 16-byte chunk kc of row r sits at
+//   kc ^ (r & 7). Fragment reads and tile writes are then bank-conflict free
+//   (measured), and every fragment address is a base register plus an
+//   immediate.
 // - v_mfma_i32_16x16x64_i8. With one group per K step (group 128) a wave's
 //   64x64 tile is worked in two 32-row halves: while one half's MFMAs run,
 //   the other half's finished group goes through its epilogue (int32 ->
@@ -37,9 +38,8 @@ namespace w4 {
 
 constexpr int kBM = 128, kBN = 128, kBK = 128;
 constexpr int kGThreads = 256;
-constexpr int kRow = 144;                          // padded LDS row, bytes
 constexpr int kStageA = kBM * kBK;                 // A rows unpadded, chunks swizzled
-constexpr int kStageB = kBN * kRow;                // B rows padded
+constexpr int kStageB = kBN * kBK;                 // B rows unpadded, chunks swizzled
 constexpr int kStage = kStageA + kStageB;
 
 enum { kModeGroup = 0, kModeChannel = 1, kModePartials = 2 };
@@ -80,20 +80,15 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // A goes straight to LDS (buffer load with the LDS destination): wave w's
   // load i fills stage rows 32w + 8i .. +7, one KiB, lane L landing at row
   // 32w + 8i + L/8, physical 16-byte chunk L%8. The lane fetches the logical
-  // chunk that belongs there under the swizzle p = kc ^ f(row), with
-  // f(row) = (row & 7) ^ ((row >> 3) & 1): 16 consecutive rows read at one
-  // logical chunk then hit distinct banks. Bit 3 of the row is i & 1, so two
-  // per-lane offsets serve all four loads.
+  // chunk that belongs there under the swizzle p = kc ^ (row & 7); row & 7 is
+  // L/8 for every load, so one per-lane offset serves all four.
   const int rows_valid = min(kBM, M - m0);
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A + (int64_t)m0 * K, (uint32_t)rows_valid * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t wrsrc =
       make_rsrc(reinterpret_cast<const uint8_t*>(Wt) + (int64_t)tn * KT * kTileBytes, (uint32_t)KT * kTileBytes);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lrow = lane >> 3, lchunk = lane & 7;
-  uint32_t a_voff[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-    a_voff[par] = (uint32_t)(32 * wave + lrow) * (uint32_t)K + 16u * (uint32_t)(lchunk ^ lrow ^ par);
+  const uint32_t a_voff = (uint32_t)(32 * wave + lrow) * (uint32_t)K + 16u * (uint32_t)(lchunk ^ lrow);
   const uint32_t w_voff = 16u * tid;                                               // units tid, tid+256
   v4i pb[2];
   auto gload = [&](int tk, auto STc) {
@@ -103,14 +98,15 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     for (int i = 0; i < 4; ++i)   // whole offset in the range-checked VGPR operand
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kStage + (32 * wave_u + 8 * i) * kBK), 16,
-          a_voff[i & 1] + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
+          a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
     const uint32_t ws = (uint32_t)tk * kTileBytes;
     pb[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws, 0);
     pb[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws + 4096u, 0);
   };
-  // B unit u (row u/4, K quarter u%4): its low nibbles unpack to K
-  // 32(u%4)+0..15, its high nibbles to +16..31 (padded rows).
-  const int b_wo = (tid >> 2) * kRow + 32 * (tid & 3);
+  // B unit u (row n = u/4, K quarter q = u%4): its low nibbles unpack to the
+  // logical chunk 2q (K 32q+0..15), its high nibbles to chunk 2q+1.
+  const int b_wo_lo = (tid >> 2) * kBK + 16 * ((2 * (tid & 3)) ^ ((tid >> 2) & 7));
+  const int b_wo_hi = (tid >> 2) * kBK + 16 * ((2 * (tid & 3) + 1) ^ ((tid >> 2) & 7));
   auto lstore_b = [&](auto STc) {
     constexpr int ST = decltype(STc)::value;
     uint8_t* lb = lds + ST * kStage + kStageA;
@@ -122,8 +118,8 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
         lo[c] = (int)(((uint32_t)pb[i][c] << 4) & 0xF0F0F0F0u);
         hi[c] = (int)((uint32_t)pb[i][c] & 0xF0F0F0F0u);
       }
-      *reinterpret_cast<v4i*>(lb + b_wo + 64 * kRow * i) = lo;
-      *reinterpret_cast<v4i*>(lb + b_wo + 64 * kRow * i + 16) = hi;
+      *reinterpret_cast<v4i*>(lb + b_wo_lo + 64 * kBK * i) = lo;
+      *reinterpret_cast<v4i*>(lb + b_wo_hi + 64 * kBK * i) = hi;
     }
   };
   // the step's A tile (LDS DMA) and B words must have landed before the barrier
@@ -188,16 +184,18 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
 
   // fragment reads: lane row (lane & 15), 16-byte chunk (lane >> 4); +64
   // bytes per 64-deep chunk and +16 rows per sub-tile are immediates
-  const int fl = (lane & 7) ^ ((lane >> 3) & 1);          // f(row) of the lane's fragment rows
+  const int fl = lane & 7;                                // row & 7 of the lane's fragment rows
   int a_ro[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) a_ro[c] = (64 * wm + (lane & 15)) * kBK + 16 * ((4 * c + (lane >> 4)) ^ fl);
-  const int b_ro = (64 * wn + (lane & 15)) * kRow + 16 * (lane >> 4);
+  int b_ro[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) b_ro[c] = (64 * wn + (lane & 15)) * kBK + 16 * ((4 * c + (lane >> 4)) ^ fl);
   auto read_b = [&](auto STc, int c, v4i (&bf)[4]) {
     constexpr int ST = decltype(STc)::value;
-    const uint8_t* lb = lds + ST * kStage + kStageA + b_ro + 64 * c;
+    const uint8_t* lb = lds + ST * kStage + kStageA + b_ro[c];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const v4i*>(lb + 16 * kRow * j);
+    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const v4i*>(lb + 16 * kBK * j);
   };
   auto mfma_rows = [&](auto STc, int c, auto I0c, auto I1c, bool fresh, const v4i (&bf)[4]) {
     constexpr int ST = decltype(STc)::value;
