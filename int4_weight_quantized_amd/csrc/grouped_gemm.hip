@@ -147,13 +147,15 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     }
     const uint8_t* la = lds + stage * kEStage;
     const uint8_t* lb = la + kEStageA;
-    const int kc = 2 * (lane >> 4);
+    // lane group g takes 16-byte chunks g and g + 4 of the K step (same
+    // order for A and B); this read pattern is bank-conflict free
+    const int kc = lane >> 4;
     v8i bf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 64 * wn + 16 * j + (lane & 15);
       const v4i x0 = *reinterpret_cast<const v4i*>(lb + eswz(row, kc));
-      const v4i x1 = *reinterpret_cast<const v4i*>(lb + eswz(row, kc + 1));
+      const v4i x1 = *reinterpret_cast<const v4i*>(lb + eswz(row, kc + 4));
       bf[j] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
     if (fresh) {
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       for (int i = 0; i < 4; ++i) {
         const int row = 64 * wm + 16 * i + (lane & 15);
         const v4i x0 = *reinterpret_cast<const v4i*>(la + eswz(row, kc));
-        const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 1));
+        const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 4));
         const v8i af = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         const v4f cinit = *reinterpret_cast<const v4f*>(&s_gs[stage][64 * wm + 16 * i + 4 * (lane >> 4)]);
 #pragma unroll
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       for (int i = 0; i < 4; ++i) {
         const int row = 64 * wm + 16 * i + (lane & 15);
         const v4i x0 = *reinterpret_cast<const v4i*>(la + eswz(row, kc));
-        const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 1));
+        const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 4));
         const v8i af = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
