@@ -67,8 +67,10 @@ __device__ __forceinline__ v4i unpack_bf16_128q(uint32_t w, uint32_t mask_s, uin
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// RT: row tiles per block; UPG: 64-wide units per group (1, 2, 4 or 8)
-template <int RT, int UPG>
+// RT: row tiles per block; UPG: 64-wide units per group (1, 2, 4 or 8);
+// MV: accumulator registers that hold real rows (M <= 4: rows sit in lanes
+// 0-15, register r = row; M > 4: all four), the epilogue skips the rest.
+template <int RT, int UPG, int MV>
 __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wt, const uint8_t* __restrict__ szt,
     uint16_t* __restrict__ out, int M, int N, int K, int NT16, int KW) {
@@ -76,46 +78,48 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, j = lane >> 4;
   const int rt0 = blockIdx.x * RT;
-  const int U = K >> 6;
-  const uint32_t kOOB = 0x80000000u;         // past every buffer: loads return 0
 
+  // Loads: a fixed per-lane VGPR offset, the tile base in the scalar offset
+  // (clamped to the last tile, so every weight and scale access is in bounds)
+  // and the unit / pair in the immediate. The
+  // activation offset keeps the window in the range-checked VGPR: rows past M
+  // and the bytes past the matrix read as zero.
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, (uint32_t)((int64_t)NT16 * KW * kWTile));
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(szt, (uint32_t)((int64_t)NT16 * KW * kSZTile));
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+  const uint32_t x_lane = (uint32_t)(l16 * K + 16 * j) * 2u;
+  const uint32_t w_lane = 16u * lane, s_lane = 32u * l16;
 
-  float y[RT][4];
+  float y[RT][MV];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[t][r] = 0.f;
+    for (int r = 0; r < MV; ++r) y[t][r] = 0.f;
   const v4i ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
   const v4f z4 = {0.f, 0.f, 0.f, 0.f};
   uint32_t mask_s, magic_v;
   asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(mask_s));
   asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic_v));
 
-  for (int kw = wave; kw < KW; kw += kDWaves) {
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar load offsets
+  for (int kw = wave_u; kw < KW; kw += kDWaves) {
     // ---- all loads of this window, in consumption order
     v4i xa[8][2];
-    const bool mv = l16 < M;
+    const uint32_t xo = x_lane + (uint32_t)kw * (kWinK * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int u = kw * 8 + i;
-        xa[i][s] = buffer_load16(xr, (mv && u < U) ? (uint32_t)((l16 * K + u * 64 + 16 * j + 8 * s) * 2) : kOOB);
-      }
+      for (int s_ = 0; s_ < 2; ++s_) xa[i][s_] = buffer_load16(xr, xo + 128u * i + 16u * s_);
     v4i wv[RT][4], szv[RT][2];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const int rt = rt0 + t;
-      const bool ok = rt < NT16;
-      const uint32_t wbase = (uint32_t)(((int64_t)rt * KW + kw) * kWTile) + 16u * lane;
+      // a tile past NT16 (last block) reloads the last tile; its rows are not stored
+      const uint32_t tile = (uint32_t)(min(rt0 + t, NT16 - 1) * KW + kw);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) wv[t][p] = buffer_load16(wr, ok ? wbase + 1024u * p : kOOB);
-      const uint32_t sbase = (uint32_t)(((int64_t)rt * KW + kw) * kSZTile) + 32u * l16;
-      szv[t][0] = buffer_load16(sr, ok ? sbase : kOOB);
-      szv[t][1] = buffer_load16(sr, ok ? sbase + 16u : kOOB);
+      for (int p = 0; p < 4; ++p)
+        wv[t][p] = __builtin_amdgcn_raw_buffer_load_b128(wr, w_lane + 1024u * p, tile * kWTile, 0);
+      szv[t][0] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_lane, tile * kSZTile, 0);
+      szv[t][1] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_lane + 16u, tile * kSZTile, 0);
     }
     __builtin_amdgcn_sched_barrier(0);       // keep the loads ahead of all compute
 
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
         if (i % UPG == UPG - 1) {
           xs[i / UPG] = run;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xinit[i / UPG][r] = -136.f * run[r];
+          for (int r = 0; r < 4; ++r) xinit[i / UPG][r] = (r < MV) ? -136.f * run[r] : 0.f;
         }
       }
     }
@@ -154,9 +158,9 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
         if (i % UPG == UPG - 1) {
           const int gi = i / UPG;                      // group slot 0..7
           const uint32_t sz = (uint32_t)szv[t][gi >> 2][gi & 3];
-          const float s = bf16_lo(sz), z = bf16_hi(sz);
+          const float s_ = bf16_lo(sz), z = bf16_hi(sz);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) y[t][r] = fmaf(s, c[r], fmaf(z, xs[gi][r], y[t][r]));
+          for (int r = 0; r < MV; ++r) y[t][r] = fmaf(s_, c[r], fmaf(z, xs[gi][r], y[t][r]));
         }
       }
     }
@@ -165,16 +169,18 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][t][lane][r] = y[t][r];
+    for (int r = 0; r < MV; ++r) red[wave][t][lane][r] = y[t][r];
   __syncthreads();
   for (int e = tid; e < RT * 256; e += kDThreads) {
     const int t = e >> 8, m = (e >> 4) & 15, nn = e & 15;   // output (m, 16*(rt0+t) + nn)
     const int l = nn + 16 * (m >> 2), r = m & 3;
-    float acc = 0.f;
-#pragma unroll
-    for (int w_ = 0; w_ < kDWaves; ++w_) acc += red[w_][t][l][r];
     const int n = 16 * (rt0 + t) + nn;
-    if (m < M && n < N) out[(int64_t)m * N + n] = f32_to_bf16_rne(acc);
+    if (m < M && n < N) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w_ = 0; w_ < kDWaves; ++w_) acc += red[w_][t][l][r];
+      out[(int64_t)m * N + n] = f32_to_bf16_rne(acc);
+    }
   }
 }
 
@@ -255,21 +261,27 @@ hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled
   const int upg = (int)(group / 64);
   // row tiles per block: enough blocks to cover ~all CUs, at most 4 tiles each
   int rt = (NT16 + 255) / 256;
-  rt = rt < 1 ? 1 : (rt > 4 ? 4 : rt);
+  rt = rt <= 1 ? 1 : (rt == 2 ? 2 : 4);
+  const int mv = M == 1 ? 1 : (M == 2 ? 2 : 4);
   dim3 grid((unsigned)((NT16 + rt - 1) / rt)), block(kDThreads);
   auto X = static_cast<const uint16_t*>(x);
   auto Wt = static_cast<const uint8_t*>(w_tiled);
   auto St = static_cast<const uint8_t*>(sz_tiled);
   auto O = static_cast<uint16_t*>(out);
   const int iM = (int)M, iN = (int)N, iK = (int)K;
-#define W4A16_LAUNCH(RT_, UPG_) \
-  hipLaunchKernelGGL((w4a16_kernel<RT_, UPG_>), grid, block, 0, stream, X, Wt, St, O, iM, iN, iK, NT16, KW)
+#define W4A16_LAUNCH(RT_, UPG_, MV_) \
+  hipLaunchKernelGGL((w4a16_kernel<RT_, UPG_, MV_>), grid, block, 0, stream, X, Wt, St, O, iM, iN, iK, NT16, KW)
+#define W4A16_MV(RT_, UPG_)                             \
+  switch (mv) {                                         \
+    case 1: W4A16_LAUNCH(RT_, UPG_, 1); break;          \
+    case 2: W4A16_LAUNCH(RT_, UPG_, 2); break;          \
+    default: W4A16_LAUNCH(RT_, UPG_, 4); break;         \
+  }
 #define W4A16_RT(UPG_)                        \
   switch (rt) {                               \
-    case 1: W4A16_LAUNCH(1, UPG_); break;     \
-    case 2: W4A16_LAUNCH(2, UPG_); break;     \
-    case 3: W4A16_LAUNCH(3, UPG_); break;     \
-    default: W4A16_LAUNCH(4, UPG_); break;    \
+    case 1: W4A16_MV(1, UPG_) break;          \
+    case 2: W4A16_MV(2, UPG_) break;          \
+    default: W4A16_MV(4, UPG_) break;         \
   }
   switch (upg) {
     case 1: W4A16_RT(1) break;
@@ -278,6 +290,7 @@ hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled
     default: W4A16_RT(8) break;
   }
 #undef W4A16_RT
+#undef W4A16_MV
 #undef W4A16_LAUNCH
   return hipGetLastError();
 }
