@@ -101,9 +101,10 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
         return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(dev)
 
-    def timed(fns, steps, warmup):
+    def timed(fns, steps, warmup, per_call=True):
         """Run the list of launch callables per step; return mean ms per callable
-        (HIP events on the launch stream), the mean step time and the wall time.
+        (HIP events on the launch stream; None without per_call), the mean
+        step time and the wall time.
         A bounded spin kernel ahead of the timed region holds the stream while
         the host enqueues every launch, so the events see back-to-back kernels
         and no host launch gaps."""
@@ -116,19 +117,21 @@ def main():
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
-        # shader-clock cycles at up to 2.4 GHz; twice the host enqueue time, at most ~0.5 s
-        torch.cuda._sleep(int(min(0.5, 2.0 * host_per_step * steps + 1e-3) * 2.4e9))
+        # shader-clock cycles at up to 2.4 GHz; twice the host enqueue time, at most ~0.1 s
+        torch.cuda._sleep(int(min(0.1, 2.0 * host_per_step * steps + 1e-3) * 2.4e9))
         t0 = time.perf_counter()
         start.record(stream)
         for s in range(steps):
-            ev[s][0].record(stream)
+            if per_call:
+                ev[s][0].record(stream)
             for i, f in enumerate(fns):
                 f()
-                ev[s][i + 1].record(stream)
+                if per_call:
+                    ev[s][i + 1].record(stream)
         end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+        per = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)])) if per_call else None
                for i in range(len(fns))]
         return per, start.elapsed_time(end) / steps, wall
 
@@ -172,8 +175,9 @@ def main():
             yd = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
             calls = [(lambda st=st: ops.w4a16_gemm(xd, st[0], st[1], gd, Nd, out=yd)) for st in sets]
             reps = max(1, args.steps // 4)
-            per, _, _ = timed(calls, reps, max(1, args.warmup // 4))
-            t = float(np.mean(per))
+            # back-to-back launches over the rotated sets: step time / launches
+            _, t_rep, _ = timed(calls, reps, max(1, args.warmup // 4), per_call=False)
+            t = t_rep / len(calls)
             nbytes = Nd * Kd // 2 + 2 * 2 * Nd * (Kd // gd) + 2 * Md * Kd + 2 * Md * Nd
             decode[f"M{Md}"] = {"us": t * 1e3, "bytes": nbytes, "gbs": nbytes / (t * 1e-3) / 1e9,
                                 "frac_hbm": nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
