@@ -137,9 +137,11 @@ int w4_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch,
  *   group     -1 (one group spanning K: per channel, [ct_w4a8] create_weights,
  *             [zentorch] can_implement) or a multiple of 64 dividing K
  *   bias      device or NULL, [N] in out_dtype
- *   out       device, [M, N] in out_dtype (W4_BF16 or W4_F16)
- * Errors: INVALID, ALIGN (K or N % 8), GROUP, DTYPE, HIP. M == 0 or N == 0
- *         enqueues nothing.
+ *   out       device, [M, N] in out_dtype (W4_BF16 or W4_F16), 16-byte
+ *             aligned (rows are written in 16-byte segments)
+ * Errors: INVALID, ALIGN (K or N % 8; w_tiled, out not 16-byte aligned; a
+ *         not 8-byte aligned), GROUP, DTYPE, HIP. M == 0 or N == 0 enqueues
+ *         nothing.
  */
 int w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled,
               const void* w_scale, int scale_dtype, int64_t group,

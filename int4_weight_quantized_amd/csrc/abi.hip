@@ -165,6 +165,7 @@ int w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled, const 
   if (rc) return rc;
   if (M == 0 || N == 0) return ok();
   if (!a_scale || !w_scale || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(out)) return fail(W4_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
   return hip_status(w4::launch_w4a8_gemm(a, a_scale, w_tiled, w_scale, group, bias, out, out_dtype == W4_BF16,
                                          nullptr, M, N, K, static_cast<hipStream_t>(stream)),
                     fn);

@@ -330,7 +330,10 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     epilogue(IC<0>{}, IC<4>{}, raw, 0);
   }
 
-  // ---- output: out = facc * a_scale / 16 + bias
+  // ---- output: out = facc * a_scale / 16 + bias. The tile goes through LDS
+  // (free after the loop's last barrier) so that each thread then writes
+  // whole 16-byte row segments: 8 vector stores per thread instead of 64
+  // 2-byte ones. N is a multiple of 8, so a segment is all in or all out.
   float bv[4] = {0.f, 0.f, 0.f, 0.f};
   if (bias) {
 #pragma unroll
@@ -344,18 +347,27 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sa[i][r] = a_scale[min(mrow0 + 16 * i + r, M - 1)] * 0.0625f;
+  constexpr int kORow = kBN * 2 + 16;                    // padded output row in LDS, bytes
+  static_assert(kBM * kORow <= 2 * kStage, "output tile fits the stage buffers");
+  const int orow0 = 64 * wm + 4 * (lane >> 4), ocol0 = 64 * wn + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mrow0 + 16 * i + r;
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int n = ncol[j];
         const float y = fmaf(facc[i][j][r], sa[i][r], bv[j]);
-        if (m < M && n < N) out[(int64_t)m * N + n] = OUT_BF16 ? f32_to_bf16_rne(y) : f32_to_f16_rne(y);
+        *reinterpret_cast<uint16_t*>(lds + (orow0 + 16 * i + r) * kORow + 2 * (ocol0 + 16 * j)) =
+            OUT_BF16 ? f32_to_bf16_rne(y) : f32_to_f16_rne(y);
       }
-    }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kBM * kBN / 8 / kGThreads; ++it) {
+    const int c = tid + kGThreads * it, row = c >> 4, seg = c & 15;
+    const int m = m0 + row, n = n0 + 8 * seg;
+    if (m < M && n < N)
+      *reinterpret_cast<v4i*>(out + (int64_t)m * N + n) = *reinterpret_cast<const v4i*>(lds + row * kORow + 16 * seg);
+  }
 }
 
 hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled,

@@ -66,6 +66,13 @@ def test_group_rules(L):
                                8, 8, 256, 256, None) == -3
 
 
+def test_output_alignment(L):
+    # the GEMM writes 16-byte row segments: a misaligned output is refused
+    p = ctypes.c_void_p
+    rc = L.w4a8_gemm(p(256), p(256), p(256), p(256), 2, 128, None, p(256 + 2), 1, 16, 256, 256, None)
+    assert rc == -2 and "out must be 16-byte aligned" in _err(L)
+
+
 def test_null_and_negative(L):
     assert L.w4a8_gemm(None, None, None, None, 2, 128, None, None, 1, 16, 256, 256, None) == -1
     assert L.w4a8_quantize_act(None, 1, -1, 256, 256, None, 4, None, None, 0, None) == -1
