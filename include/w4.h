@@ -202,11 +202,12 @@ int w4a16_gemm(const void* x, const void* w_tiled, const void* sz_tiled, int64_t
  *   expert_offsets device, int32 [E+1], non-decreasing, [0] = 0, [E] = R
  *   w_tiled     device, E tiled matrices (w4_repack with batch = E)
  *   w_scale     device, fp16 [E, G, N]
- *   group       a multiple of 128 dividing K
+ *   group       128, 256 or 512, dividing K
  *   out         device, bf16 [R, N], rows in segment order
- * Errors: INVALID, ALIGN, GROUP, DTYPE, HIP. Offsets and token ids are read
- * on the device and are not validated; out-of-range values are undefined
- * behaviour.
+ *   a, w_tiled and out must be 16-byte aligned.
+ * Errors: INVALID, ALIGN, GROUP, DTYPE, UNSUPPORTED (T*K >= 2^31), HIP.
+ * Offsets and token ids are read on the device and are not validated;
+ * out-of-range values are undefined behaviour.
  */
 int w4a8_grouped_gemm(const void* a, int a_dtype, const float* a_scale,
                       const float* a_group_sums, const int32_t* row_token,

@@ -249,11 +249,13 @@ int w4a8_grouped_gemm(const void* a, int a_dtype, const float* a_scale, const fl
     return fail(W4_ERR_GROUP, "%s: group size %lld must be 128, 256 or 512 and divide K=%lld", fn, (long long)group,
                 (long long)K);
   if (R == 0 || N == 0 || E == 0) return ok();
-  if (T <= 0 || (int64_t)T * K >= ((int64_t)1 << 35))
-    return fail(W4_ERR_UNSUPPORTED, "%s: token count T=%lld out of range for K=%lld", fn, (long long)T, (long long)K);
+  if (T <= 0 || (int64_t)T * K >= ((int64_t)1 << 31))
+    return fail(W4_ERR_UNSUPPORTED, "%s: token count T=%lld out of range for K=%lld (T*K must be below 2^31)", fn,
+                (long long)T, (long long)K);
   if (!a || !a_scale || !a_group_sums || !row_token || !expert_offsets || !w_tiled || !w_scale || !out)
     return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
-  if (!aligned16(a) || !aligned16(w_tiled)) return fail(W4_ERR_ALIGN, "%s: a and w_tiled must be 16-byte aligned", fn);
+  if (!aligned16(a) || !aligned16(w_tiled) || !aligned16(out))
+    return fail(W4_ERR_ALIGN, "%s: a, w_tiled and out must be 16-byte aligned", fn);
   return hip_status(w4::launch_grouped_fp8(a, a_scale, a_group_sums, row_token, expert_offsets, E, w_tiled,
                                            w4::tiled_bytes(K, N), w_scale, group, out, T, R, N, K,
                                            static_cast<hipStream_t>(stream)),

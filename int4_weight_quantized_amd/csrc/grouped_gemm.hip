@@ -15,11 +15,22 @@
 //   group starts from C[m][.] = -8 * sum_{k in g} a[t_m,k] (row sums written
 //   by the activation quantizer), so D = sum_k a*(q-8) for every column.
 // - The group's fp16 scale is applied with one FMA per output into fp32
-//   accumulators; the token scale at the end; bf16 output in row order.
+//   accumulators; the token scale at the end.
 // - Block tile 128 rows x 128 columns, 4 waves of 64x64, K step 128, two LDS
-//   stages; activation rows are gathered by token id while staging to LDS.
+//   stages. Activation rows are gathered by token id straight into LDS (LDS
+//   DMA: each lane's source row is its token's); rows past the segment read
+//   as zero. B comes through registers, 8 KiB contiguous per tile, and is
+//   unpacked once per block. 16-byte LDS chunks are swizzled by row & 7 and
+//   lane group g reads chunks g and g + 4: bank-conflict free.
+// - A two-half schedule like the W4A8 kernel's (epilogue of one half under
+//   the other half's MFMAs) does not fit the registers here: the fp8
+//   fragments are twice as wide, and it spills. The epilogue follows each
+//   group's last MFMAs.
 // - Work items (expert, row tile, column tile) are enumerated on the device
 //   from expert_offsets; the grid is an upper bound and idle blocks exit.
+//   The output tile goes through LDS and leaves as 16-byte row segments.
+#include <type_traits>
+
 #include "w4_device.h"
 
 namespace w4 {
@@ -28,16 +39,16 @@ constexpr int kEM = 128, kEN = 128, kEK = 128;
 constexpr int kEThreads = 256;
 constexpr int kEStageA = kEM * kEK, kEStageB = kEN * kEK, kEStage = kEStageA + kEStageB;
 
-__device__ __forceinline__ int eswz(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
+template <int V>
+using EC = std::integral_constant<int, V>;
 
 // GT: K steps (of 128) per weight group (group = 128 * GT)
 template <int GT>
 __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ a_scale, const float* __restrict__ gsum,
     const int32_t* __restrict__ row_token, const int32_t* __restrict__ offsets, int E,
-    const v4i* __restrict__ Wt, int64_t w_stride16, const uint16_t* __restrict__ wscale,
-    uint16_t* __restrict__ out, int N, int K, int KT, int NT) {
-  constexpr int group_tiles = GT;
+    const uint8_t* __restrict__ Wt, int64_t w_stride, const uint16_t* __restrict__ wscale,
+    uint16_t* __restrict__ out, int N, int K, int KT, int NT, int T) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kEStage];
   __shared__ int s_tok[kEM];                       // token of each row of the tile (-1: none)
   __shared__ __attribute__((aligned(16))) float s_gs[2][kEM];   // -8 * row sum of the staged group
@@ -61,44 +72,62 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   }
   if (e < 0) return;                       // idle block (grid is an upper bound)
 
-  const int G = K / (group_tiles * kEK);
+  const int G = K / (GT * kEK);
   const int r0 = mt * kEM, n0 = tn * kEN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  // ---- staging: activation rows gathered by token
   if (tid < kEM) s_tok[tid] = (r0 + tid < cnt) ? row_token[seg0 + r0 + tid] : -1;
   __syncthreads();
-  const int arow0 = tid >> 3, akc = tid & 7;
-  const uint8_t* abase = A + 16 * akc;
-  const v4i* wexp = Wt + (int64_t)e * w_stride16;
-  v4i pa[4], pb[2];
+
+  // ---- loads. A: wave w's DMA i fills stage rows 32w + 8i .. +7 (one KiB),
+  // lane L landing at row 32w + 8i + L/8, physical chunk L%8, and fetching
+  // the logical chunk (L%8) ^ (L/8) of its row's token. A row without a
+  // token gets an offset past the buffer, which reads as zero. Offsets stay
+  // in the range-checked VGPR operand (T*K < 2^31, checked by the caller).
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A, (uint32_t)((int64_t)T * K));
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  uint32_t a_voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = s_tok[32 * wave + 8 * i + lrow];
+    a_voff[i] = (tok >= 0) ? (uint32_t)tok * (uint32_t)K + 16u * (uint32_t)(lchunk ^ lrow) : 0x80000000u;
+  }
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      make_rsrc(Wt + (int64_t)e * w_stride + (int64_t)tn * KT * kTileBytes, (uint32_t)KT * kTileBytes);
+  const uint32_t w_voff = 16u * tid;                   // units tid, tid + 256
+  // group sums of the tile rows (threads 0..127, one row each); a row
+  // without a token reads past the buffer (zero)
+  const __amdgpu_buffer_rsrc_t gsrc = make_rsrc(gsum, (uint32_t)((int64_t)T * G * 4));
+  const int my_tok = (tid < kEM) ? s_tok[tid] : -1;
+  const uint32_t g_voff = (my_tok >= 0) ? (uint32_t)my_tok * (uint32_t)G * 4u : 0x80000000u;
+  v4i pb[2];
   float pgs = 0.f;
-  auto gload = [&](int tk) {
+  auto gload = [&](int tk, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    const uint32_t ks = (uint32_t)tk * kEK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tk_ = s_tok[arow0 + 32 * i];          // LDS read: no live register per row
-      const v4i v = *reinterpret_cast<const v4i*>(abase + (int64_t)max(tk_, 0) * K + (int64_t)tk * kEK);
-      pa[i] = (tk_ >= 0) ? v : v4i{0, 0, 0, 0};
-    }
-    const v4i* wt = wexp + (((int64_t)tn * KT + tk) << 9);
-    pb[0] = wt[tid];
-    pb[1] = wt[tid + kEThreads];
-    if (tid < kEM && (tk % group_tiles) == 0) {
-      const int tk_ = s_tok[tid];
-      const float v = gsum[(int64_t)max(tk_, 0) * G + tk / group_tiles];   // clamped: no branch
-      pgs = (tk_ >= 0) ? -8.f * v : 0.f;
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kEStage + (32 * wave_u + 8 * i) * kEK), 16,
+          a_voff[i] + ks, 0, 0, 0);
+    const uint32_t ws = (uint32_t)tk * kTileBytes;
+    pb[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws, 0);
+    pb[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws + 4096u, 0);
+    if (wave_u < 2 && (tk % GT) == 0)
+      pgs = -8.f * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, g_voff + 4u * (uint32_t)(tk / GT), 0, 0));
   };
-  auto lstore = [&](int stage, int tk) {
-    uint8_t* la = lds + stage * kEStage;
-    uint8_t* lb = la + kEStageA;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i*>(la + eswz(arow0 + 32 * i, akc)) = pa[i];
-    if (tid < kEM && (tk % group_tiles) == 0) s_gs[stage][tid] = pgs;
+  // B unit u (row n = u/4, K quarter q = u%4): low nibbles -> logical chunk
+  // 2q (K 32q+0..15), high nibbles -> chunk 2q+1, as fp8 codes q.
+  const int b_wo_lo = (tid >> 2) * kEK + 16 * ((2 * (tid & 3)) ^ ((tid >> 2) & 7));
+  const int b_wo_hi = (tid >> 2) * kEK + 16 * ((2 * (tid & 3) + 1) ^ ((tid >> 2) & 7));
+  auto lstore = [&](auto STc, int tk) {
+    constexpr int ST = decltype(STc)::value;
+    uint8_t* lb = lds + ST * kEStage + kEStageA;
+    if (wave_u < 2 && (tk % GT) == 0) s_gs[ST][tid] = pgs;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int u = tid + kEThreads * i, nl = u >> 2, kq = u & 3;
       v4i lo, hi;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -106,108 +135,149 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
         lo[c] = (int)(x & 0x0F0F0F0Fu);
         hi[c] = (int)((x >> 4) & 0x0F0F0F0Fu);
       }
-      *reinterpret_cast<v4i*>(lb + eswz(nl, 2 * kq)) = lo;
-      *reinterpret_cast<v4i*>(lb + eswz(nl, 2 * kq + 1)) = hi;
+      *reinterpret_cast<v4i*>(lb + b_wo_lo + 64 * kEK * i) = lo;
+      *reinterpret_cast<v4i*>(lb + b_wo_hi + 64 * kEK * i) = hi;
     }
   };
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0): the DMA tile landed
 
-  // ---- per-lane output rows / columns
+  // ---- scales of group g (fp16, low half of each register), clamped columns
   const int ncol0 = n0 + 64 * wn + (lane & 15);    // column of fragment j: ncol0 + 16 j
-  // scales of the group that ends in a K step, fetched one step ahead
-  uint16_t scr[4];
-  auto fetch_scales = [&](int tk) {
-    const int g = tk / group_tiles;
+  const __amdgpu_buffer_rsrc_t srsrc = make_rsrc(wscale + (int64_t)e * G * N, (uint32_t)((int64_t)G * N * 2));
+  uint32_t s_voff[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) scr[j] = wscale[((int64_t)e * G + g) * N + min(ncol0 + 16 * j, N - 1)];
+  for (int j = 0; j < 4; ++j) s_voff[j] = 2u * (uint32_t)min(ncol0 + 16 * j, N - 1);
+  auto fetch_scales = [&](int g, uint32_t (&raw)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      raw[j] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, s_voff[j], (uint32_t)g * (uint32_t)N * 2u, 0);
   };
+
   v4f acc[4][4];
   float facc[4][4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 4; ++r) facc[i][j][r] = 0.f;
+    }
+  auto epilogue = [&](auto I0c, auto I1c, const uint32_t (&raw)[4]) {
+    constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sc = f16_to_f32((uint16_t)raw[j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) facc[i][j][r] = fmaf(acc[i][j][r], sc, facc[i][j][r]);
+      }
+  };
 
-  gload(0);
-  fetch_scales(0);
-  lstore(0, 0);
+  // ---- fragments: lane row (lane & 15), lane group g = lane >> 4 takes the
+  // 16-byte chunks g and g + 4 of the K step (same order for A and B)
+  const int fl = lane & 7, g4 = lane >> 4;
+  const int a_ro0 = (64 * wm + (lane & 15)) * kEK + 16 * (g4 ^ fl);
+  const int a_ro1 = (64 * wm + (lane & 15)) * kEK + 16 * ((g4 + 4) ^ fl);
+  const int b_ro0 = (64 * wn + (lane & 15)) * kEK + 16 * (g4 ^ fl);
+  const int b_ro1 = (64 * wn + (lane & 15)) * kEK + 16 * ((g4 + 4) ^ fl);
+  auto frag = [&](const uint8_t* base, int o0, int o1) -> v8i {
+    const v4i x0 = *reinterpret_cast<const v4i*>(base + o0);
+    const v4i x1 = *reinterpret_cast<const v4i*>(base + o1);
+    return v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  };
+  auto read_a = [&](auto STc, int i) -> v8i {
+    constexpr int ST = decltype(STc)::value;
+    return frag(lds + ST * kEStage + 16 * kEK * i, a_ro0, a_ro1);
+  };
+  auto read_b = [&](auto STc, v8i (&bf)[4]) {
+    constexpr int ST = decltype(STc)::value;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = frag(lds + ST * kEStage + kEStageA + 16 * kEK * j, b_ro0, b_ro1);
+  };
+  auto read_cinit = [&](auto STc, int i) -> v4f {
+    constexpr int ST = decltype(STc)::value;
+    return *reinterpret_cast<const v4f*>(&s_gs[ST][64 * wm + 16 * i + 4 * g4]);
+  };
+  auto mfma_row = [&](int i, const v8i& af, const v8i (&bf)[4], const v4f& c0, bool fresh) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], fresh ? c0 : acc[i][j], 0, 0, 0, 127,
+                                                                   0, 136);
+  };
+
+  // ---- prologue
+  gload(0, EC<0>{});
+  lstore(EC<0>{}, 0);
+  wait_loads();
   __syncthreads();
-  for (int tk = 0; tk < KT; ++tk) {
-    const int stage = tk & 1;
-    const bool more = tk + 1 < KT;
-    const bool fresh = (tk % group_tiles) == 0;
-    const bool last = (tk % group_tiles) == group_tiles - 1;
-    float sc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j] = f16_to_f32(scr[j]);
-    if (more) {
-      gload(tk + 1);
-      fetch_scales(tk + 1);
-    }
-    const uint8_t* la = lds + stage * kEStage;
-    const uint8_t* lb = la + kEStageA;
-    // lane group g takes 16-byte chunks g and g + 4 of the K step (same
-    // order for A and B); this read pattern is bank-conflict free
-    const int kc = lane >> 4;
+
+  // K step tk reads stage ST = tk & 1 while tile tk + 1 streams into the
+  // other stage (A by DMA, B through registers stored at the end of the
+  // step). Past the last tile the loads repeat it: the body is branch-free.
+  auto kstep = [&](int tk, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    gload(min(tk + 1, KT - 1), EC<ST ^ 1>{});
+    const bool fresh = (tk % GT) == 0, last = (tk % GT) == GT - 1;
+    uint32_t sc[4];
+    fetch_scales(tk / GT, sc);
     v8i bf[4];
+    read_b(EC<ST>{}, bf);
+    // one row's A fragment and C init at a time (bounds the live registers)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 64 * wn + 16 * j + (lane & 15);
-      const v4i x0 = *reinterpret_cast<const v4i*>(lb + eswz(row, kc));
-      const v4i x1 = *reinterpret_cast<const v4i*>(lb + eswz(row, kc + 4));
-      bf[j] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    for (int i = 0; i < 4; ++i) {
+      mfma_row(i, read_a(EC<ST>{}, i), bf, read_cinit(EC<ST>{}, i), fresh);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (fresh) {
-      // first K step of a group: the accumulator starts at -8 * row sum
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wm + 16 * i + (lane & 15);
-        const v4i x0 = *reinterpret_cast<const v4i*>(la + eswz(row, kc));
-        const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 4));
-        const v8i af = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        const v4f cinit = *reinterpret_cast<const v4f*>(&s_gs[stage][64 * wm + 16 * i + 4 * (lane >> 4)]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], cinit, 0, 0, 0, 127, 0, 136);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wm + 16 * i + (lane & 15);
-        const v4i x0 = *reinterpret_cast<const v4i*>(la + eswz(row, kc));
-        const v4i x1 = *reinterpret_cast<const v4i*>(la + eswz(row, kc + 4));
-        const v8i af = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 127, 0, 136);
-      }
-    }
-    if (last) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) facc[i][j][r] = fmaf(acc[i][j][r], sc[j], facc[i][j][r]);
-    }
-    if (more) lstore(stage ^ 1, tk + 1);
+    if (last) epilogue(EC<0>{}, EC<4>{}, sc);
+    lstore(EC<ST ^ 1>{}, tk + 1);
+    wait_loads();
     __syncthreads();
+  };
+
+  // (the two loop shapes are equivalent; each is the one the register
+  // allocator handles without spills for its group size)
+  if constexpr (GT == 4) {
+    int tk = 0;
+    for (; tk + 1 < KT; tk += 2) {
+      kstep(tk, EC<0>{});
+      kstep(tk + 1, EC<1>{});
+    }
+    if (tk < KT) kstep(tk, EC<0>{});
+  } else {
+    for (int tk = 0; tk < KT; ++tk) {
+      if (tk & 1) kstep(tk, EC<1>{});
+      else kstep(tk, EC<0>{});
+    }
   }
 
+  // ---- output: row scale, bf16, staged through LDS (free after the last
+  // barrier) and written as 16-byte row segments (N is a multiple of 8)
+  constexpr int kORow = kEN * 2 + 16;
+  static_assert(kEM * kORow <= 2 * kEStage, "output tile fits the stage buffers");
+  const int orow0 = 64 * wm + 4 * g4, ocol0 = 64 * wn + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int lr = 64 * wm + 16 * i + 4 * (lane >> 4) + r;
-      const int tk_ = s_tok[lr];
-      if (tk_ < 0) continue;
-      const int rr = seg0 + r0 + lr;
-      const float sa = a_scale[tk_];
+      const int tok = s_tok[orow0 + 16 * i + r];
+      const float sa = a_scale[max(tok, 0)];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (ncol0 + 16 * j < N) out[(int64_t)rr * N + ncol0 + 16 * j] = f32_to_bf16_rne(facc[i][j][r] * sa);
+        *reinterpret_cast<uint16_t*>(lds + (orow0 + 16 * i + r) * kORow + 2 * (ocol0 + 16 * j)) =
+            f32_to_bf16_rne(facc[i][j][r] * sa);
     }
+  __syncthreads();
+  const int rows = min(kEM, cnt - r0);
+#pragma unroll
+  for (int it = 0; it < kEM * kEN / 8 / kEThreads; ++it) {
+    const int c = tid + kEThreads * it, row = c >> 4, seg = c & 15;
+    const int n = n0 + 8 * seg;
+    if (row < rows && n < N)
+      *reinterpret_cast<v4i*>(out + (int64_t)(seg0 + r0 + row) * N + n) =
+          *reinterpret_cast<const v4i*>(lds + row * kORow + 16 * seg);
+  }
 }
 
 hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* gsum,
@@ -215,23 +285,22 @@ hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* 
                               const void* w_tiled, size_t w_bytes_per_expert, const void* w_scale,
                               int64_t group, void* out, int64_t T, int64_t R, int64_t N, int64_t K,
                               hipStream_t stream) {
-  (void)T;
   if (R == 0 || N == 0 || E == 0) return hipSuccess;
   const int KT = (int)(K / kEK), NT = (int)((N + kEN - 1) / kEN);
   const int64_t upper = ((R + kEM - 1) / kEM + E) * NT;
   dim3 grid((unsigned)upper), block(kEThreads);
   auto Ap = static_cast<const uint8_t*>(a);
-  auto Wp = static_cast<const v4i*>(w_tiled);
+  auto Wp = static_cast<const uint8_t*>(w_tiled);
   auto Sp = static_cast<const uint16_t*>(w_scale);
   auto Op = static_cast<uint16_t*>(out);
-  const int64_t ws = (int64_t)(w_bytes_per_expert / 16);
+  const int64_t ws = (int64_t)w_bytes_per_expert;
   switch (group / kEK) {
     case 1: hipLaunchKernelGGL((grouped_fp8_kernel<1>), grid, block, 0, stream, Ap, a_scale, gsum, row_token, offsets,
-                               (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT); break;
+                               (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT, (int)T); break;
     case 2: hipLaunchKernelGGL((grouped_fp8_kernel<2>), grid, block, 0, stream, Ap, a_scale, gsum, row_token, offsets,
-                               (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT); break;
+                               (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT, (int)T); break;
     default: hipLaunchKernelGGL((grouped_fp8_kernel<4>), grid, block, 0, stream, Ap, a_scale, gsum, row_token, offsets,
-                                (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT); break;
+                                (int)E, Wp, ws, Sp, Op, (int)N, (int)K, KT, NT, (int)T); break;
   }
   return hipGetLastError();
 }
