@@ -272,7 +272,9 @@ def _moe_run(d):
 
 
 @pytest.mark.parametrize("E,K,N,group,T,topk", [
-    (4, 256, 64, 128, 32, 2), (1, 384, 8, 128, 16, 1), (8, 512, 136, 256, 300, 3), (16, 128, 128, 128, 5, 2)])
+    (4, 256, 64, 128, 32, 2), (1, 384, 8, 128, 16, 1), (8, 512, 136, 256, 300, 3), (16, 128, 128, 128, 5, 2),
+    (2, 1024, 64, 512, 40, 2),       # group 512 (four K steps per group)
+    (2, 256, 72, 128, 300, 2)])      # ~300 rows per expert: several row tiles, ragged last tile
 def test_grouped_small(E, K, N, group, T, topk):
     d = W.moe_inputs(E, K, N, group, T, topk, seed=E * 100 + T)
     a8, s, y = _moe_run(d)
