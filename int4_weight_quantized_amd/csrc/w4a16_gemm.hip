@@ -31,9 +31,13 @@
 //     y += scale*C + zero*XS.
 // - A 512-thread block owns RT row tiles; its 8 waves take the 8 windows of a
 //   4096-wide K pass and keep that pass's activations in registers for all
-//   RT tiles. All loads of a pass are issued up front in the order they are
-//   consumed (raw buffer loads: masked rows/units read as zero); partial
-//   tiles of the 8 waves are summed through LDS.
+//   RT tiles. A pass loads the activations and the first tile up front, then
+//   issues each next tile's weight and scale loads just before it computes
+//   the current one (raw buffer loads: masked rows/units read as zero). One
+//   tile in flight per wave keeps the stream going and lets each tile's
+//   unpack overlap the next tile's transfer; issuing every tile at once made
+//   all of them arrive late together. Partial tiles of the 8 waves are
+//   summed through LDS.
 #include "w4_device.h"
 
 namespace w4 {
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar load offsets
   for (int kw = wave_u; kw < KW; kw += kDWaves) {
-    // ---- all loads of this window, in consumption order
+    // ---- activations of this window, then the first row tile
     v4i xa[8][2];
     const uint32_t xo = x_lane + (uint32_t)kw * (kWinK * 2);
 #pragma unroll
@@ -111,8 +115,7 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
 #pragma unroll
       for (int s_ = 0; s_ < 2; ++s_) xa[i][s_] = buffer_load16(xr, xo + 128u * i + 16u * s_);
     v4i wv[RT][4], szv[RT][2];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
+    auto load_tile = [&](int t) {
       // a tile past NT16 (last block) reloads the last tile; its rows are not stored
       const uint32_t tile = (uint32_t)(min(rt0 + t, NT16 - 1) * KW + kw);
 #pragma unroll
@@ -120,8 +123,9 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
         wv[t][p] = __builtin_amdgcn_raw_buffer_load_b128(wr, w_lane + 1024u * p, tile * kWTile, 0);
       szv[t][0] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_lane, tile * kSZTile, 0);
       szv[t][1] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_lane + 16u, tile * kSZTile, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);       // keep the loads ahead of all compute
+    };
+    load_tile(0);
+    __builtin_amdgcn_sched_barrier(0);       // keep these loads ahead of all compute
 
     // ---- activation row sums per group (shared by the row tiles): XS of
     // group gi in xs[gi]; the group's product accumulator starts at -136*XS
@@ -144,6 +148,8 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
     // ---- row tiles
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
+      if (t + 1 < RT) load_tile(t + 1);        // next tile in flight while this one computes
+      __builtin_amdgcn_sched_barrier(0);
       v4f c = z4;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
