@@ -29,22 +29,24 @@
 //   come from the MFMA against ones; the group's product accumulator starts
 //   at -136*XS, so it ends at sum_k x*(q-8), and per group
 //     y += scale*C + zero*XS.
-// - A 512-thread block owns RT row tiles; its 8 waves take the 8 windows of a
-//   4096-wide K pass and keep that pass's activations in registers for all
+// - A 1024-thread block owns RT row tiles; its 16 waves take the two halves
+//   of the 8 windows of a 4096-wide K pass (fewer than 128 VGPRs each, so
+//   four waves share a SIMD) and keep their activations in registers for all
 //   RT tiles. A pass loads the activations and the first tile up front, then
 //   issues each next tile's weight and scale loads just before it computes
 //   the current one (raw buffer loads: masked rows/units read as zero). One
 //   tile in flight per wave keeps the stream going and lets each tile's
 //   unpack overlap the next tile's transfer; issuing every tile at once made
-//   all of them arrive late together. Partial tiles of the 8 waves are
+//   all of them arrive late together. Partial tiles of the 16 waves are
 //   summed through LDS.
 #include "w4_device.h"
 
 namespace w4 {
 
-constexpr int kDThreads = 512;
-constexpr int kDWaves = kDThreads / kWave;
+constexpr int kDThreads = 512;             // one wave per window of a 4096-wide pass
+constexpr int kDWaves = kDThreads / kWave; // windows per pass
 constexpr int kWinK = 512;                 // K per window (8 units of 64)
+constexpr int kWPW = 2;                    // waves per window
 constexpr int kWTile = 4096;               // weight bytes per (row tile, window)
 constexpr int kSZTile = 16 * 8 * 2 * 2;    // scale/zero bytes per (row tile, window)
 
@@ -73,26 +75,38 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // RT: row tiles per block; UPG: 64-wide units per group (1, 2, 4 or 8);
 // MV: accumulator registers that hold real rows (M <= 4: rows sit in lanes
-// 0-15, register r = row; M > 4: all four), the epilogue skips the rest.
-template <int RT, int UPG, int MV>
-__global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
+// 0-15, register r = row; M > 4: all four), the epilogue skips the rest;
+// WPW: waves per 512-wide window (1 or 2): each wave takes UPW = 8/WPW units
+// of its window. The epilogue is linear in a group's partial sums, so a group
+// split between two waves is finished by each wave on its own part.
+template <int RT, int UPG, int MV, int WPW>
+__global__ __launch_bounds__(kDThreads * WPW, 1) void w4a16_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wt, const uint8_t* __restrict__ szt,
     uint16_t* __restrict__ out, int M, int N, int K, int NT16, int KW) {
-  __shared__ __attribute__((aligned(16))) float red[kDWaves][RT][kWave][4];
+  constexpr int NW = kDWaves * WPW;                 // waves per block
+  constexpr int UPW = 8 / WPW;                      // units per wave and window
+  constexpr int PPW = UPW / 2;                      // 1 KiB unit pairs per wave and tile
+  constexpr int NG = UPW >= UPG ? UPW / UPG : 1;    // groups (or group parts) per wave
+  constexpr int NSZ = (NG + 3) / 4;                 // 16-byte scale/zero registers per tile
+  __shared__ __attribute__((aligned(16))) float red[NW][RT][kWave][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, j = lane >> 4;
   const int rt0 = blockIdx.x * RT;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar load offsets
+  const int u0 = (wave_u % WPW) * UPW;                        // first unit of this wave in a window
 
   // Loads: a fixed per-lane VGPR offset, the tile base in the scalar offset
   // (clamped to the last tile, so every weight and scale access is in bounds)
-  // and the unit / pair in the immediate. The
-  // activation offset keeps the window in the range-checked VGPR: rows past M
-  // and the bytes past the matrix read as zero.
+  // and the pair in the immediate. The activation offset keeps the window in
+  // the range-checked VGPR: rows past M and the bytes past the matrix read as
+  // zero. The scale/zero load starts at this wave's first group slot, so slot
+  // i/UPG of the register belongs to local unit i.
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, (uint32_t)((int64_t)NT16 * KW * kWTile));
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(szt, (uint32_t)((int64_t)NT16 * KW * kSZTile));
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
-  const uint32_t x_lane = (uint32_t)(l16 * K + 16 * j) * 2u;
-  const uint32_t w_lane = 16u * lane, s_lane = 32u * l16;
+  const uint32_t x_lane = (uint32_t)(l16 * K + 16 * j + 64 * u0) * 2u;
+  const uint32_t w_lane = 16u * lane + 512u * (uint32_t)u0;
+  const uint32_t s_lane = 32u * l16 + 4u * (uint32_t)(u0 / UPG);
 
   float y[RT][MV];
 #pragma unroll
@@ -105,39 +119,42 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
   asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(mask_s));
   asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic_v));
 
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar load offsets
-  for (int kw = wave_u; kw < KW; kw += kDWaves) {
-    // ---- activations of this window, then the first row tile
-    v4i xa[8][2];
+  auto first_of_group = [](int i) { return i % UPG == 0; };
+  auto last_of_group = [](int i) { return i % UPG == UPG - 1 || i == UPW - 1; };
+
+  for (int kw = wave_u / WPW; kw < KW; kw += kDWaves) {
+    // ---- activations of this wave's units, then the first row tile
+    v4i xa[UPW][2];
     const uint32_t xo = x_lane + (uint32_t)kw * (kWinK * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < UPW; ++i)
 #pragma unroll
       for (int s_ = 0; s_ < 2; ++s_) xa[i][s_] = buffer_load16(xr, xo + 128u * i + 16u * s_);
-    v4i wv[RT][4], szv[RT][2];
+    v4i wv[RT][PPW], szv[RT][NSZ];
     auto load_tile = [&](int t) {
       // a tile past NT16 (last block) reloads the last tile; its rows are not stored
       const uint32_t tile = (uint32_t)(min(rt0 + t, NT16 - 1) * KW + kw);
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
+      for (int p = 0; p < PPW; ++p)
         wv[t][p] = __builtin_amdgcn_raw_buffer_load_b128(wr, w_lane + 1024u * p, tile * kWTile, 0);
-      szv[t][0] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_lane, tile * kSZTile, 0);
-      szv[t][1] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_lane + 16u, tile * kSZTile, 0);
+#pragma unroll
+      for (int q = 0; q < NSZ; ++q)
+        szv[t][q] = __builtin_amdgcn_raw_buffer_load_b128(sr, s_lane + 16u * q, tile * kSZTile, 0);
     };
     load_tile(0);
     __builtin_amdgcn_sched_barrier(0);       // keep these loads ahead of all compute
 
     // ---- activation row sums per group (shared by the row tiles): XS of
-    // group gi in xs[gi]; the group's product accumulator starts at -136*XS
-    v4f xs[8], xinit[8];
+    // local group gi in xs[gi]; the group's product accumulator starts at -136*XS
+    v4f xs[NG], xinit[NG];
     {
       v4f run = z4;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < UPW; ++i) {
         const v4f a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]), as_v8bf(ones),
-                                                              (i % UPG == 0) ? z4 : run, 0, 0, 0);
+                                                              first_of_group(i) ? z4 : run, 0, 0, 0);
         run = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]), as_v8bf(ones), a, 0, 0, 0);
-        if (i % UPG == UPG - 1) {
+        if (last_of_group(i)) {
           xs[i / UPG] = run;
 #pragma unroll
           for (int r = 0; r < 4; ++r) xinit[i / UPG][r] = (r < MV) ? -136.f * run[r] : 0.f;
@@ -152,17 +169,17 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
       __builtin_amdgcn_sched_barrier(0);
       v4f c = z4;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < UPW; ++i) {
         const uint32_t w0 = (uint32_t)wv[t][i >> 1][(i & 1) * 2];
         const uint32_t w1 = (uint32_t)wv[t][i >> 1][(i & 1) * 2 + 1];
         // c = sum_k x*(128+q) - 136*XS = sum_k x*(q-8) over the group
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]),
                                                     as_v8bf(unpack_bf16_128q(w0, mask_s, magic_v)),
-                                                    (i % UPG == 0) ? xinit[i / UPG] : c, 0, 0, 0);
+                                                    first_of_group(i) ? xinit[i / UPG] : c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]),
                                                     as_v8bf(unpack_bf16_128q(w1, mask_s, magic_v)), c, 0, 0, 0);
-        if (i % UPG == UPG - 1) {
-          const int gi = i / UPG;                      // group slot 0..7
+        if (last_of_group(i)) {
+          const int gi = i / UPG;                      // local group slot
           const uint32_t sz = (uint32_t)szv[t][gi >> 2][gi & 3];
           const float s_ = bf16_lo(sz), z = bf16_hi(sz);
 #pragma unroll
@@ -177,14 +194,14 @@ __global__ __launch_bounds__(kDThreads, 1) void w4a16_kernel(
 #pragma unroll
     for (int r = 0; r < MV; ++r) red[wave][t][lane][r] = y[t][r];
   __syncthreads();
-  for (int e = tid; e < RT * 256; e += kDThreads) {
+  for (int e = tid; e < RT * 256; e += kDThreads * WPW) {
     const int t = e >> 8, m = (e >> 4) & 15, nn = e & 15;   // output (m, 16*(rt0+t) + nn)
     const int l = nn + 16 * (m >> 2), r = m & 3;
     const int n = 16 * (rt0 + t) + nn;
     if (m < M && n < N) {
       float acc = 0.f;
 #pragma unroll
-      for (int w_ = 0; w_ < kDWaves; ++w_) acc += red[w_][t][l][r];
+      for (int w_ = 0; w_ < NW; ++w_) acc += red[w_][t][l][r];
       out[(int64_t)m * N + n] = f32_to_bf16_rne(acc);
     }
   }
@@ -269,14 +286,14 @@ hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled
   int rt = (NT16 + 255) / 256;
   rt = rt <= 1 ? 1 : (rt == 2 ? 2 : 4);
   const int mv = M == 1 ? 1 : (M == 2 ? 2 : 4);
-  dim3 grid((unsigned)((NT16 + rt - 1) / rt)), block(kDThreads);
+  dim3 grid((unsigned)((NT16 + rt - 1) / rt));
   auto X = static_cast<const uint16_t*>(x);
   auto Wt = static_cast<const uint8_t*>(w_tiled);
   auto St = static_cast<const uint8_t*>(sz_tiled);
   auto O = static_cast<uint16_t*>(out);
   const int iM = (int)M, iN = (int)N, iK = (int)K;
 #define W4A16_LAUNCH(RT_, UPG_, MV_) \
-  hipLaunchKernelGGL((w4a16_kernel<RT_, UPG_, MV_>), grid, block, 0, stream, X, Wt, St, O, iM, iN, iK, NT16, KW)
+  hipLaunchKernelGGL((w4a16_kernel<RT_, UPG_, MV_, kWPW>), grid, dim3(kDThreads * kWPW), 0, stream, X, Wt, St, O, iM, iN, iK, NT16, KW)
 #define W4A16_MV(RT_, UPG_)                             \
   switch (mv) {                                         \
     case 1: W4A16_LAUNCH(RT_, UPG_, 1); break;          \
