@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--only", choices=["all", "w4a8", "decode", "moe"], default="all")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    p.add_argument("--crossover", action="store_true",
+                   help="time both paths of w4_linear over a range of row counts on the up-projection "
+                        "weights and print that table instead of the benchmark line")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run three plain 1 GiB device-to-device copies: the known-size kernel that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -158,6 +161,29 @@ def main():
         "gemm_tops": tops_gemm, "gemm_frac_int8_peak": tops_gemm / PEAK_INT8_TOPS,
         "quant_gbs": quant_bytes / (t_q * 1e-3) / 1e9,
     }
+
+    if args.crossover:
+        # both dispatch targets on the same tiled weights, rotated over copies
+        # larger together than the 256 MB MALL so that weights stream from HBM
+        nrot = 12
+        wts = [ops.w4_repack(qw.roll(i, 1).contiguous(), ops.W4_LAYOUT_GPTQ_KN, K, N) for i in range(nrot)]
+        table = []
+        for Mc in (1, 2, 4, 8, 16, 24, 32, 48, 64, 80, 96, 112, 128, 192, 256, 384, 512):
+            xc = x[:Mc]
+            yc = torch.empty((Mc, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty((ops.w4_linear_workspace_bytes(Mc, K, 1),), dtype=torch.uint8, device=dev)
+            f_wo = [(lambda w=w: ops.w4_linear(xc, w, sc, g, N, min_tokens_int8=1 << 30, out=yc)) for w in wts]
+            f_i8 = [(lambda w=w: ops.w4_linear(xc, w, sc, g, N, min_tokens_int8=1, out=yc, workspace=ws))
+                    for w in wts]
+            reps = max(2, args.steps // 10)
+            _, t_wo, _ = timed(f_wo, reps, 2, per_call=False)
+            _, t_i8, _ = timed(f_i8, reps, 2, per_call=False)
+            table.append({"M": Mc, "weight_only_us": t_wo / nrot * 1e3, "int8_us": t_i8 / nrot * 1e3})
+            print(json.dumps(table[-1]), flush=True)
+        cross = next((r["M"] for r in table if r["int8_us"] < r["weight_only_us"]), None)
+        print(json.dumps({"crossover": {"workload": f"w4_linear K={K} N={N} group={g} bf16", "table": table,
+                                        "first_M_int8_faster": cross}}), flush=True)
+        return
 
     # ------------------------------------------------------------ W4A16 decode
     decode = {}

@@ -216,6 +216,49 @@ int w4a8_grouped_gemm(const void* a, int a_dtype, const float* a_scale,
                       int64_t group, void* out, int out_dtype,
                       int64_t T, int64_t R, int64_t N, int64_t K, void* stream);
 
+/*
+ * Weight-only int4 GEMM for few rows on the kernel-tiled weights of w4a8_gemm
+ * (the same bytes and the same fp16 scales), activations unquantized.
+ * [inc_w4a8] class docstring: the int8 kernel and the weight-only kernel take
+ * bit-identical weights; apply_weights: below a token-count threshold the
+ * layer calls the weight-only path instead of quantizing the activations.
+ *   out[m,n] = sum_g w_scale[g,n] * sum_{k in g} x[m,k] * (q[k,n] - 8) + bias[n]
+ *   x         device, [M, K] contiguous, bf16 or fp16 (x_dtype); 8-byte aligned
+ *   w_tiled   device, from w4_repack (16-byte aligned)
+ *   w_scale   device, fp16 [G, N]; scale_dtype must be W4_F16
+ *   group     -1 or a multiple of 64 dividing K (as w4a8_gemm)
+ *   bias      device or NULL, [N] in the activation dtype
+ *   out       device, [M, N] in the activation dtype
+ * Errors: INVALID, ALIGN (K, N % 8; pointers), GROUP, DTYPE,
+ *         UNSUPPORTED (M > 16), HIP.
+ */
+int w4a16_tiled_gemm(const void* x, int x_dtype, const void* w_tiled, const void* w_scale,
+                     int scale_dtype, int64_t group, const void* bias, void* out,
+                     int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * The linear layer with its per-call dispatch ([inc_w4a8] apply_weights and
+ * _MIN_TOKENS_FOR_INT8): M >= min_tokens_int8 quantizes the activations per
+ * token to int8 (w4a8_quantize_act) and runs w4a8_gemm; fewer rows run the
+ * weight-only path (w4a16_tiled_gemm, 16 rows per launch). Both read the same
+ * tiled weights and fp16 scales.
+ *   min_tokens_int8  threshold; <= 0 selects W4_LINEAR_MIN_TOKENS_INT8, the
+ *             crossover measured on MI355X for these kernels (the page's 512
+ *             was measured for its own device)
+ *   workspace device scratch of at least w4_linear_workspace_bytes(M, K,
+ *             min_tokens_int8) bytes (16-byte aligned; may be NULL when that
+ *             is 0): int8 codes and fp32 row scales of the int8 path. The
+ *             caller owns it; calls sharing one workspace must not overlap.
+ *   x, out    device, 16-byte aligned; out [M, N] in the activation dtype
+ *   other arguments as w4a16_tiled_gemm.
+ * Errors: those of the path taken, and INVALID when the workspace is too small.
+ */
+#define W4_LINEAR_MIN_TOKENS_INT8 33
+int w4_linear_workspace_bytes(int64_t M, int64_t K, int64_t min_tokens_int8, size_t* bytes);
+int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_scale, int scale_dtype,
+              int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
+              int64_t min_tokens_int8, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* w4_last_error(void);
 

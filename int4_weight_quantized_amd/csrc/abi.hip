@@ -22,6 +22,8 @@ hipError_t launch_w4a16_repack(const uint8_t* w, const void* scale, const void* 
                                int64_t N, void* w_tiled, void* sz_tiled, hipStream_t stream);
 hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled, int64_t group, void* out,
                         int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_w4a16_tiled(const void* x, bool f16, const void* w_tiled, const void* w_scale, int64_t group,
+                              const void* bias, void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* gsum, const int32_t* row_token,
                               const int32_t* offsets, int64_t E, const void* w_tiled, size_t w_bytes_per_expert,
                               const void* w_scale, int64_t group, void* out, int64_t T, int64_t R, int64_t N,
@@ -81,7 +83,7 @@ extern "C" {
 
 const char* w4_last_error(void) { return g_err; }
 
-int w4_version(void) { return 100; }
+int w4_version(void) { return 101; }
 
 int w4a8_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, void* codes,
                       int code_dtype, float* scales, float* group_sums, int64_t group, void* stream) {
@@ -259,6 +261,88 @@ int w4a8_grouped_gemm(const void* a, int a_dtype, const float* a_scale, const fl
   return hip_status(w4::launch_grouped_fp8(a, a_scale, a_group_sums, row_token, expert_offsets, E, w_tiled,
                                            w4::tiled_bytes(K, N), w_scale, group, out, T, R, N, K,
                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+static int check_tiled(const char* fn, const void* x, int x_dtype, const void* w_tiled, const void* w_scale,
+                       int scale_dtype, int64_t group, int64_t M, int64_t N, int64_t K) {
+  if (x_dtype != W4_BF16 && x_dtype != W4_F16)
+    return fail(W4_ERR_DTYPE, "%s: activations must be bf16 or fp16 (dtype code %d)", fn, x_dtype);
+  if (scale_dtype != W4_F16)
+    return fail(W4_ERR_DTYPE, "%s: weight scales must be fp16 (dtype code %d)", fn, scale_dtype);
+  int rc = check_mnk(fn, M, N, K);
+  if (rc) return rc;
+  if (group != -1 && (group <= 0 || group % 64 || K % group))
+    return fail(W4_ERR_GROUP, "%s: group size %lld must be -1 (per channel) or a multiple of 64 dividing K=%lld", fn,
+                (long long)group, (long long)K);
+  if (M == 0 || N == 0) return W4_OK;
+  if (!x || !w_tiled || !w_scale) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(w_tiled)) return fail(W4_ERR_ALIGN, "%s: w_tiled must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(x) & 7u) != 0) return fail(W4_ERR_ALIGN, "%s: x must be 8-byte aligned", fn);
+  return W4_OK;
+}
+
+int w4a16_tiled_gemm(const void* x, int x_dtype, const void* w_tiled, const void* w_scale, int scale_dtype,
+                     int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K, void* stream) {
+  const char* fn = "w4a16_tiled_gemm";
+  int rc = check_tiled(fn, x, x_dtype, w_tiled, w_scale, scale_dtype, group, M, N, K);
+  if (rc) return rc;
+  if (M > 16) return fail(W4_ERR_UNSUPPORTED, "%s: M=%lld > 16 (the kernel takes up to 16 rows)", fn, (long long)M);
+  if (M == 0 || N == 0) return ok();
+  if (!out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  return hip_status(w4::launch_w4a16_tiled(x, x_dtype == W4_F16, w_tiled, w_scale, group, bias, out, M, N, K,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+static int64_t linear_threshold(int64_t t) { return t > 0 ? t : W4_LINEAR_MIN_TOKENS_INT8; }
+
+// int8 codes first (rounded up to 256 bytes), then the fp32 row scales
+static size_t linear_workspace(int64_t M, int64_t K, int64_t t) {
+  if (M < linear_threshold(t)) return 0;
+  return (((size_t)M * (size_t)K + 255) & ~(size_t)255) + (size_t)M * 4;
+}
+
+int w4_linear_workspace_bytes(int64_t M, int64_t K, int64_t min_tokens_int8, size_t* bytes) {
+  const char* fn = "w4_linear_workspace_bytes";
+  if (!bytes) return fail(W4_ERR_INVALID, "%s: null output pointer", fn);
+  if (M < 0 || K <= 0) return fail(W4_ERR_INVALID, "%s: sizes must be M >= 0, K > 0", fn);
+  *bytes = linear_workspace(M, K, min_tokens_int8);
+  return ok();
+}
+
+int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_scale, int scale_dtype, int64_t group,
+              const void* bias, void* out, int64_t M, int64_t N, int64_t K, int64_t min_tokens_int8, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  const char* fn = "w4_linear";
+  int rc = check_tiled(fn, x, x_dtype, w_tiled, w_scale, scale_dtype, group, M, N, K);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return ok();
+  if (!out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(out) || !aligned16(x)) return fail(W4_ERR_ALIGN, "%s: x and out must be 16-byte aligned", fn);
+  const size_t need = linear_workspace(M, K, min_tokens_int8);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(W4_ERR_INVALID, "%s: workspace of %zu bytes is smaller than the %zu needed for M=%lld K=%lld", fn,
+                workspace_bytes, need, (long long)M, (long long)K);
+  if (need && !aligned16(workspace)) return fail(W4_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool f16 = x_dtype == W4_F16;
+  if (M < linear_threshold(min_tokens_int8)) {
+    // weight-only path, 16 rows per launch
+    for (int64_t m0 = 0; m0 < M; m0 += 16) {
+      const int64_t rows = M - m0 < 16 ? M - m0 : 16;
+      rc = hip_status(w4::launch_w4a16_tiled(static_cast<const uint16_t*>(x) + m0 * K, f16, w_tiled, w_scale, group,
+                                             bias, static_cast<uint16_t*>(out) + m0 * N, rows, N, K, st),
+                      fn);
+      if (rc) return rc;
+    }
+    return ok();
+  }
+  int8_t* codes = static_cast<int8_t*>(workspace);
+  float* scales = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + (need - (size_t)M * 4));
+  rc = hip_status(w4::launch_quant_act(x, !f16, M, K, K, codes, false, scales, nullptr, 0, st), fn);
+  if (rc) return rc;
+  return hip_status(w4::launch_w4a8_gemm(codes, scales, w_tiled, w_scale, group, bias, out, !f16, nullptr, M, N, K, st),
                     fn);
 }
 

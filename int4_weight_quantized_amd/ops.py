@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libw4.so")
 
 W4_BF16, W4_F16, W4_F32, W4_I8, W4_FP8_E4M3 = 1, 2, 3, 4, 5
 W4_LAYOUT_GPTQ_KN, W4_LAYOUT_CT_NK, W4_LAYOUT_S4_NK = 1, 2, 3
+W4_LINEAR_MIN_TOKENS_INT8 = 33          # include/w4.h: the library's default dispatch threshold
 ERRORS = {0: "OK", -1: "INVALID", -2: "ALIGN", -3: "GROUP", -4: "DTYPE", -5: "UNSUPPORTED", -6: "HIP"}
 
 _lib = None
@@ -31,6 +32,9 @@ _SIGS = {
     "w4a16_repack": [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _P],
     "w4a16_gemm": [_P, _P, _P, _I64, _P, _I64, _I64, _I64, _P],
     "w4a8_grouped_gemm": [_P, _I, _P, _P, _P, _P, _I64, _P, _P, _I, _I64, _P, _I, _I64, _I64, _I64, _I64, _P],
+    "w4a16_tiled_gemm": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _P],
+    "w4_linear_workspace_bytes": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+    "w4_linear": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
     "w4_last_error": [],
     "w4_version": [],
 }
@@ -185,6 +189,40 @@ def w4a8_grouped_gemm(a8, a_scale, a_group_sums, row_token, expert_offsets, w_ti
     _check("w4a8_grouped_gemm", lib().w4a8_grouped_gemm(
         _ptr(a8), W4_FP8_E4M3, _ptr(a_scale), _ptr(a_group_sums), _ptr(row_token), _ptr(expert_offsets),
         E, _ptr(w_tiled), _ptr(w_scale), W4_F16, group, _ptr(out), W4_BF16, T, R, N, K, _stream(stream)))
+    return out
+
+
+def w4a16_tiled_gemm(x, w_tiled, w_scale, group: int, N: int, bias=None, out=None, stream=None):
+    """Weight-only path on the w4_repack tiles: x [M <= 16, K] bf16/fp16 -> out [M, N] (x dtype)."""
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check("w4a16_tiled_gemm", lib().w4a16_tiled_gemm(
+        _ptr(x), _half_code(x.dtype), _ptr(w_tiled), _ptr(w_scale), W4_F16 if w_scale.dtype == torch.float16 else W4_BF16,
+        group, _ptr(bias), _ptr(out), M, N, K, _stream(stream)))
+    return out
+
+
+def w4_linear_workspace_bytes(M: int, K: int, min_tokens_int8: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check("w4_linear_workspace_bytes", lib().w4_linear_workspace_bytes(M, K, min_tokens_int8, ctypes.byref(n)))
+    return n.value
+
+
+def w4_linear(x, w_tiled, w_scale, group: int, N: int, bias=None, min_tokens_int8: int = 0, out=None,
+              workspace=None, stream=None):
+    """The layer with its per-call dispatch: int8 path from min_tokens_int8 rows up (<= 0: the library's
+    default), weight-only path below. The workspace (uint8, device) is allocated here if not given."""
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    need = w4_linear_workspace_bytes(M, K, min_tokens_int8)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    _check("w4_linear", lib().w4_linear(
+        _ptr(x), _half_code(x.dtype), _ptr(w_tiled), _ptr(w_scale), W4_F16 if w_scale.dtype == torch.float16 else W4_BF16,
+        group, _ptr(bias), _ptr(out), M, N, K, min_tokens_int8, _ptr(workspace) if need else None,
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
     return out
 
 

@@ -267,6 +267,26 @@ def w4a8_reference(x_bits, x_dtype, qweight, scales_f16, group, bias_bits=None, 
 
 
 # --------------------------------------------------------------------------
+# Weight-only path on the GPTQ weights ([inc_w4a8] class docstring: the int8
+# and the weight-only kernels take bit-identical weights; apply_weights: below
+# _MIN_TOKENS_FOR_INT8 tokens the layer runs the weight-only path). The
+# activations stay unquantized; the weight of (k, n) is (q - 8) * scale[g, n].
+# --------------------------------------------------------------------------
+
+
+def w4a16_gptq_reference(x_bits, x_dtype, qweight, scales_gn, group, bias_bits=None) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * (q[k, n] - 8) * scale[k // g, n] (+ bias[n]), float64."""
+    x = half_bits_to_f32(x_bits, x_dtype).astype(np.float64)
+    W = unpack_gptq_kn(qweight).astype(np.float64) - 8.0            # [K, N]
+    g = effective_group(group, W.shape[0])
+    S = np.repeat(np.asarray(scales_gn, dtype=np.float64), g, axis=0)  # [K, N]
+    y = x @ (W * S)
+    if bias_bits is not None:
+        y += half_bits_to_f32(bias_bits, x_dtype).astype(np.float64)[None, :]
+    return y
+
+
+# --------------------------------------------------------------------------
 # W4A16 ([cpu_int4] module docstring and CPUInt4EmbeddingMethod.embedding):
 # bf16 activations, weights w = (q - 8) * scale + zero with bf16 scale and
 # zero per (output row, group), codes two per byte low nibble first.

@@ -301,3 +301,48 @@ def test_grouped_moe_workload():
     ref = O.grouped_fp8_reference(rc, rs, d["row_token"], off, d["w"], d["scales"], d["group"], rows=rows)
     assert_close(to_f64(y[torch.from_numpy(rows).to(DEV)]), ref, "moe sample")
     assert torch.isfinite(y.float()).all()
+
+
+# ------------------------------------------------------------------ weight-only path on the tiled weights
+
+def _tiled_weights(d):
+    wt = ops.w4_repack(torch.from_numpy(d["qweight"]).to(DEV), ops.W4_LAYOUT_GPTQ_KN, d["K"], d["N"])
+    sc = torch.from_numpy(np.ascontiguousarray(d["scales"])).to(DEV)
+    return wt, sc
+
+
+@pytest.mark.parametrize("M,K,N,group,dtype,bias", [
+    (1, 4096, 14336, 128, "bf16", False), (8, 4096, 14336, 128, "bf16", True), (16, 256, 256, 128, "bf16", False),
+    (3, 192, 24, 64, "f16", True), (5, 1024, 264, -1, "bf16", False), (1, 8192, 136, 512, "f16", False),
+    (13, 14336, 72, 256, "bf16", True), (2, 200, 40, -1, "f16", False), (16, 4096, 1000, 64, "f16", True),
+    (4, 4352, 4104, 128, "bf16", False)])
+def test_w4a16_tiled(M, K, N, group, dtype, bias):
+    d = W.w4a8_inputs(M, K, N, group, dtype, seed=7 * M + K + N, with_bias=bias)
+    print(f"\n[w4a16 tiled] M={M} K={K} N={N} g={group} {dtype} bias={bias}", flush=True)
+    wt, sc = _tiled_weights(d)
+    x = dev_half(d["x"], dtype)
+    b = dev_half(d["bias"], dtype) if bias else None
+    y = ops.w4a16_tiled_gemm(x, wt, sc, group, N, bias=b)
+    assert y.dtype == x.dtype
+    ref = O.w4a16_gptq_reference(d["x"], dtype, d["qweight"], d["scales"], group, bias_bits=d["bias"])
+    assert_close(to_f64(y), ref, f"w4a16 tiled {M}x{K}x{N} g{group} {dtype}")
+
+
+@pytest.mark.parametrize("M,threshold", [(20, 32), (20, 8), (1, 0), (40, 0)])
+def test_w4_linear_dispatch(M, threshold):
+    """Both sides of the per-call dispatch on the same tiled weights: the
+    weight-only path (16 rows per launch) below the threshold, per-token int8
+    quantization + W4A8 GEMM from it up."""
+    K, N, group = 1024, 520, 128
+    d = W.w4a8_inputs(M, K, N, group, "bf16", seed=M + 101 * threshold, with_bias=True)
+    print(f"\n[w4_linear] M={M} threshold={threshold}", flush=True)
+    wt, sc = _tiled_weights(d)
+    x = dev_half(d["x"], "bf16")
+    b = dev_half(d["bias"], "bf16")
+    y = ops.w4_linear(x, wt, sc, group, N, bias=b, min_tokens_int8=threshold)
+    t = threshold if threshold > 0 else ops.W4_LINEAR_MIN_TOKENS_INT8
+    if M < t:
+        ref = O.w4a16_gptq_reference(d["x"], "bf16", d["qweight"], d["scales"], group, bias_bits=d["bias"])
+    else:
+        ref = O.w4a8_reference(d["x"], "bf16", d["qweight"], d["scales"], group, bias_bits=d["bias"])["y"]
+    assert_close(to_f64(y), ref, f"w4_linear M={M} threshold={threshold}")

@@ -29,14 +29,15 @@ def L():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for must in ("w4a8_quantize_act", "w4a8_gemm", "w4a16_gemm", "w4a16_repack", "w4a8_grouped_gemm", "w4_repack",
-                 "w4_repack_bytes", "w4a8_gemm_partials", "w4_last_error", "w4_version"):
+                 "w4_repack_bytes", "w4a8_gemm_partials", "w4a16_tiled_gemm", "w4_linear", "w4_linear_workspace_bytes",
+                 "w4_last_error", "w4_version"):
         assert must in names
 
 
 def test_library_exports_every_declared_symbol(L):
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert L.w4_version() == 100
+    assert L.w4_version() == 101
 
 
 def _err(L):
@@ -104,3 +105,21 @@ def test_repack_bytes(L):
     assert n.value == 4096 * 14336 // 2
     assert L.w4_repack_bytes(200, 8, ctypes.byref(n)) == 0
     assert n.value == 2 * 1 * 8192               # padded to 128 x 128 tiles
+
+
+def test_linear_workspace_and_dispatch_checks(L):
+    n = ctypes.c_size_t()
+    assert L.w4_linear_workspace_bytes(10, 4096, 0, ctypes.byref(n)) == 0 and n.value == 0   # weight-only
+    assert L.w4_linear_workspace_bytes(64, 4096, 0, ctypes.byref(n)) == 0
+    assert n.value == 64 * 4096 + 64 * 4                                                      # codes + scales
+    assert L.w4_linear_workspace_bytes(100, 200, 0, ctypes.byref(n)) == 0
+    assert n.value == (100 * 200 + 255) // 256 * 256 + 100 * 4
+    assert L.w4_linear_workspace_bytes(64, 4096, 65, ctypes.byref(n)) == 0 and n.value == 0   # own threshold
+    p = ctypes.c_void_p
+    # too small a workspace for the int8 path is refused before any launch
+    rc = L.w4_linear(p(256), 1, p(256), p(256), 2, 128, None, p(256), 64, 256, 4096, 0, None, 0, None)
+    assert rc == -1 and "workspace" in _err(L)
+    # the weight-only kernel takes at most 16 rows; fp16 scales only
+    assert L.w4a16_tiled_gemm(p(256), 1, p(256), p(256), 2, 128, None, p(256), 17, 256, 4096, None) == -5
+    assert L.w4a16_tiled_gemm(p(256), 1, p(256), p(256), 1, 128, None, p(256), 4, 256, 4096, None) == -4
+    assert L.w4a16_tiled_gemm(p(256), 1, p(256), p(256), 2, 96, None, p(256), 4, 256, 4096, None) == -3

@@ -387,3 +387,60 @@ def test_grouped_single_expert_is_dense():
     q = O.unpack_ct_nk(d["w"][0]).astype(np.float64) - 8
     Wd = q * np.repeat(d["scales"][0].astype(np.float64), 128, axis=0).T
     assert np.allclose(y, A @ Wd.T, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ weight-only path on GPTQ weights
+
+def test_w4a16_gptq_reduces_to_byte_layout_path():
+    """Same codes in the GPTQ words and in the two-per-byte layout, zero offsets
+    0 and scales representable in both fp16 and bf16: the weight-only GPTQ
+    reference equals the (separately pinned) byte-layout reference."""
+    rng = np.random.default_rng(41)
+    M, K, N, g = 3, 256, 24, 64
+    xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q = rng.integers(0, 16, (K, N))
+    words = np.zeros((K // 8, N), dtype=np.uint32)
+    for i in range(8):
+        words |= (q[i::8, :].astype(np.uint32) << np.uint32(4 * i))
+    s = (rng.integers(1, 128, (K // g, N)) * 2.0 ** -12).astype(np.float32)   # exact in fp16 and bf16
+    y = O.w4a16_gptq_reference(xb, "bf16", words.view(np.int32), s.astype(np.float16), g)
+    wbytes = O.pack_nibble_bytes(q.T.astype(np.uint8))                        # [N, K/2]
+    sb = (s.T.copy().view(np.uint32) >> 16).astype(np.uint16)
+    zb = np.zeros_like(sb)
+    ref = O.w4a16_reference(xb, wbytes, sb, zb, g)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_w4a16_gptq_one_hot_and_bias():
+    rng = np.random.default_rng(42)
+    K, N, g = 128, 16, 64
+    words = rng.integers(0, 2**32, (K // 8, N), dtype=np.uint32).view(np.int32)
+    s = rng.uniform(0.005, 0.02, (K // g, N)).astype(np.float16)
+    k = 77
+    x = np.zeros((1, K), dtype=np.float32)
+    x[0, k] = 3.0
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    y = O.w4a16_gptq_reference(xb, "bf16", words, s, g)[0]
+    qk = (words.view(np.uint32)[k // 8] >> np.uint32(4 * (k % 8))) & 15
+    assert np.array_equal(y, 3.0 * (qk.astype(np.float64) - 8) * s[k // g].astype(np.float64))
+    bias = (np.arange(N, dtype=np.float32) / 8).astype(np.float16).view(np.uint16)
+    xh = x.astype(np.float16).view(np.uint16)
+    yb = O.w4a16_gptq_reference(xh, "f16", words, s, g, bias_bits=bias)[0]
+    assert np.array_equal(yb, y + np.arange(N) / 8)
+
+
+def test_w4a16_gptq_brute_force_per_channel():
+    rng = np.random.default_rng(43)
+    M, K, N = 2, 24, 8
+    words = rng.integers(0, 2**32, (K // 8, N), dtype=np.uint32)
+    s = rng.uniform(0.005, 0.02, (1, N)).astype(np.float16)
+    xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = O.w4a16_gptq_reference(xb, "bf16", words.view(np.int32), s, -1)
+    x = O.bf16_bits_to_f32(xb).astype(np.float64)
+    for m in range(M):
+        for n in range(N):
+            tot = 0.0
+            for kk in range(K):
+                code = (int(words[kk // 8, n]) >> (4 * (kk % 8))) & 15
+                tot += x[m, kk] * (code - 8) * float(s[0, n])
+            assert abs(y[m, n] - tot) <= 1e-12 * max(1.0, abs(tot))
