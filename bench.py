@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--only", choices=["all", "w4a8", "decode", "moe"], default="all")
+    p.add_argument("--only", choices=["all", "w4a8", "decode", "moe", "vocab"], default="all")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     p.add_argument("--crossover", action="store_true",
                    help="time both paths of w4_linear over a range of row counts on the up-projection "
@@ -234,6 +234,41 @@ def main():
                "gemm_frac_fp8_peak": flops / (t_gg * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
         del wm
 
+    # ------------------------------------------------------------ int4 vocab table (tied embedding / head)
+    vocab = {}
+    if args.only in ("all", "vocab"):
+        V, Kv, gv, Tv = 131072, 2048, 64, 8192
+        rng = np.random.default_rng(1006)
+        table = torch.from_numpy(rng.standard_normal((V, Kv), dtype=np.float32) * np.float32(0.02)).to(dev)
+        table = table.to(torch.bfloat16)
+        fqg = lambda: ops.w4_quantize_groupwise(table, gv, torch.bfloat16)
+        _, t_qg, _ = timed([fqg], max(2, args.steps // 10), 2, per_call=False)
+        packed, sv, zv = fqg()
+        del table
+        sets = []
+        for i in range(3):                  # 3 x 150 MB of tiles: more than the MALL
+            sets.append(ops.w4a16_repack(packed.roll(i, 0).contiguous(), sv.roll(i, 0).contiguous(),
+                                         zv.roll(i, 0).contiguous(), gv))
+        ids = torch.from_numpy(rng.integers(0, V, Tv).astype(np.int32)).to(dev)
+        emb = torch.empty((Tv, Kv), dtype=torch.bfloat16, device=dev)
+        f_emb = [(lambda st=st: ops.w4a16_embedding(ids, st[0], st[1], gv, V, Kv, out=emb)) for st in sets]
+        _, t_emb, _ = timed(f_emb, max(2, args.steps // 5), 2, per_call=False)
+        xh = torch.from_numpy(rng.standard_normal((1, Kv), dtype=np.float32)).to(dev).to(torch.bfloat16)
+        yh = torch.empty((1, V), dtype=torch.bfloat16, device=dev)
+        f_head = [(lambda st=st: ops.w4a16_gemm(xh, st[0], st[1], gv, V, out=yh)) for st in sets]
+        _, t_head, _ = timed(f_head, max(2, args.steps // 5), 2, per_call=False)
+        t_emb, t_head = t_emb / len(sets), t_head / len(sets)
+        Gv = Kv // gv
+        qg_bytes = V * Kv * 2 + V * Kv // 2 + 2 * 2 * V * Gv
+        emb_bytes = Tv * (Kv // 2 + 4 * Gv + 4 + 2 * Kv)
+        head_bytes = V * Kv // 2 + 4 * V * Gv + 2 * Kv + 2 * V
+        vocab = {"workload": f"int4 vocab table V={V} K={Kv} group={gv}; embedding T={Tv}; tied head M=1",
+                 "quantize_groupwise_us": t_qg * 1e3, "quantize_groupwise_gbs": qg_bytes / (t_qg * 1e-3) / 1e9,
+                 "embedding_us": t_emb * 1e3, "embedding_gbs": emb_bytes / (t_emb * 1e-3) / 1e9,
+                 "head_us": t_head * 1e3, "head_gbs": head_bytes / (t_head * 1e-3) / 1e9,
+                 "head_frac_hbm": head_bytes / (t_head * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del sets, packed, sv, zv
+
     # ------------------------------------------------------------ roofline of the dominant kernel
     achieved = ops_gemm / (t_g * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
@@ -253,7 +288,7 @@ def main():
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": w4a8["workload"], "global_batch": M, "seq_len": 1, "parallelism": "single_gpu",
                    "step": "w4a8_quantize_act + w4a8_gemm"},
-        "w4a8": w4a8, "decode": decode, "moe": moe,
+        "w4a8": w4a8, "decode": decode, "moe": moe, "vocab": vocab,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

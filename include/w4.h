@@ -259,6 +259,39 @@ int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_sca
               int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
               int64_t min_tokens_int8, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Groupwise min/max int4 quantization of a weight matrix, on the device.
+ * [cpu_int4] quantize_groupwise: per row n and group g of `group` columns, in
+ * fp32: scale = max(max - min, 1e-9) / 15, zero = min + 8 * scale,
+ * q = clamp(rne((w - min) / scale), 0, 15), so that (q - 8) * scale + zero
+ * reproduces the group's min and max; codes two per byte, low nibble first
+ * ([cpu_int4] pack_nibbles), the byte layout that w4a16_repack reads.
+ *   w        device, [N, K] contiguous, bf16, fp16 or fp32 (w_dtype);
+ *            16-byte aligned
+ *   group    64, 128, 256 or 512, dividing K
+ *   packed   device, uint8 [N, K/2], 4-byte aligned
+ *   scale, zero  device, [N, K/group] each, fp32 or bf16 (sz_dtype; bf16 is
+ *            the fp32 value rounded to nearest even)
+ * Errors: INVALID, ALIGN (pointers), GROUP, DTYPE, HIP. Any N (rows are
+ *         independent); w4a16_repack then needs N % 8 == 0.
+ */
+int w4_quantize_groupwise(const void* w, int w_dtype, int64_t N, int64_t K, int64_t group,
+                          uint8_t* packed, void* scale, void* zero, int sz_dtype, void* stream);
+
+/*
+ * Int4 embedding gather. [cpu_int4] CPUInt4EmbeddingMethod.embedding: the rows
+ * of the vocab table picked by the token ids, dequantized as
+ * (q - 8) * scale + zero in fp32 and cast to bf16. The table is read in the
+ * W4A16 tiled layout, so the same w_tiled / sz_tiled serve the tied output
+ * head (w4a16_gemm) ([cpu_int4] tie_weights shares every quantized tensor).
+ *   ids      device, int32 [T]; an id outside [0, V) yields a zero row
+ *   w_tiled, sz_tiled  from w4a16_repack of the [V, K] table with this group
+ *   out      device, bf16 [T, K], 16-byte aligned
+ * Errors: INVALID, ALIGN, GROUP, UNSUPPORTED (V*K >= 2^31), HIP.
+ */
+int w4a16_embedding(const int32_t* ids, int64_t T, const void* w_tiled, const void* sz_tiled,
+                    int64_t group, int64_t V, int64_t K, void* out, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* w4_last_error(void);
 

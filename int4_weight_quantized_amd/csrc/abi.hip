@@ -24,6 +24,10 @@ hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled
                         int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_w4a16_tiled(const void* x, bool f16, const void* w_tiled, const void* w_scale, int64_t group,
                               const void* bias, void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_quantize_groupwise(const void* w, int w_dtype_code, int64_t N, int64_t K, int64_t group,
+                                     void* packed, void* scale, void* zero, bool sz_bf16, hipStream_t stream);
+hipError_t launch_embedding(const int32_t* ids, int64_t T, const void* w_tiled, const void* sz_tiled, int64_t group,
+                            int64_t V, int64_t K, void* out, hipStream_t stream);
 hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* gsum, const int32_t* row_token,
                               const int32_t* offsets, int64_t E, const void* w_tiled, size_t w_bytes_per_expert,
                               const void* w_scale, int64_t group, void* out, int64_t T, int64_t R, int64_t N,
@@ -343,6 +347,43 @@ int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_sca
   rc = hip_status(w4::launch_quant_act(x, !f16, M, K, K, codes, false, scales, nullptr, 0, st), fn);
   if (rc) return rc;
   return hip_status(w4::launch_w4a8_gemm(codes, scales, w_tiled, w_scale, group, bias, out, !f16, nullptr, M, N, K, st),
+                    fn);
+}
+
+int w4_quantize_groupwise(const void* w, int w_dtype, int64_t N, int64_t K, int64_t group, uint8_t* packed,
+                          void* scale, void* zero, int sz_dtype, void* stream) {
+  const char* fn = "w4_quantize_groupwise";
+  if (w_dtype != W4_BF16 && w_dtype != W4_F16 && w_dtype != W4_F32)
+    return fail(W4_ERR_DTYPE, "%s: weights must be bf16, fp16 or fp32 (dtype code %d)", fn, w_dtype);
+  if (sz_dtype != W4_F32 && sz_dtype != W4_BF16)
+    return fail(W4_ERR_DTYPE, "%s: scale and zero must be fp32 or bf16 (dtype code %d)", fn, sz_dtype);
+  // rows are independent: any N; K is split into whole groups
+  if (N < 0 || K <= 0 || N > kMaxDim || K > ((int64_t)1 << 24))
+    return fail(W4_ERR_INVALID, "%s: sizes out of range (N=%lld K=%lld)", fn, (long long)N, (long long)K);
+  if (group != 64 && group != 128 && group != 256 && group != 512)
+    return fail(W4_ERR_GROUP, "%s: group size %lld must be 64, 128, 256 or 512", fn, (long long)group);
+  if (K % group) return fail(W4_ERR_GROUP, "%s: group size %lld does not divide K=%lld", fn, (long long)group, (long long)K);
+  if (N == 0) return ok();
+  if (!w || !packed || !scale || !zero) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(w) || (reinterpret_cast<uintptr_t>(packed) & 3u))
+    return fail(W4_ERR_ALIGN, "%s: w must be 16-byte and packed 4-byte aligned", fn);
+  const int code = w_dtype == W4_BF16 ? 0 : (w_dtype == W4_F16 ? 1 : 2);
+  return hip_status(w4::launch_quantize_groupwise(w, code, N, K, group, packed, scale, zero, sz_dtype == W4_BF16,
+                                                  static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int w4a16_embedding(const int32_t* ids, int64_t T, const void* w_tiled, const void* sz_tiled, int64_t group,
+                    int64_t V, int64_t K, void* out, void* stream) {
+  const char* fn = "w4a16_embedding";
+  if (T < 0 || V < 0) return fail(W4_ERR_INVALID, "%s: negative size (T=%lld V=%lld)", fn, (long long)T, (long long)V);
+  int rc = check_w4a16(fn, group, V, K);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if (!ids || !w_tiled || !sz_tiled || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(w_tiled) || !aligned16(sz_tiled) || !aligned16(out))
+    return fail(W4_ERR_ALIGN, "%s: w_tiled, sz_tiled and out must be 16-byte aligned", fn);
+  return hip_status(w4::launch_embedding(ids, T, w_tiled, sz_tiled, group, V, K, out, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -35,6 +35,8 @@ _SIGS = {
     "w4a16_tiled_gemm": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _P],
     "w4_linear_workspace_bytes": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "w4_linear": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
+    "w4_quantize_groupwise": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P],
+    "w4a16_embedding": [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P],
     "w4_last_error": [],
     "w4_version": [],
 }
@@ -223,6 +225,29 @@ def w4_linear(x, w_tiled, w_scale, group: int, N: int, bias=None, min_tokens_int
         _ptr(x), _half_code(x.dtype), _ptr(w_tiled), _ptr(w_scale), W4_F16 if w_scale.dtype == torch.float16 else W4_BF16,
         group, _ptr(bias), _ptr(out), M, N, K, min_tokens_int8, _ptr(workspace) if need else None,
         workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def w4_quantize_groupwise(w, group: int, sz_dtype=torch.float32, stream=None):
+    """w [N, K] bf16/fp16/fp32 -> (packed uint8 [N, K/2], scale [N, K/group], zero [N, K/group])."""
+    N, K = w.shape
+    wdt = {torch.bfloat16: W4_BF16, torch.float16: W4_F16, torch.float32: W4_F32}[w.dtype]
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((N, K // group), dtype=sz_dtype, device=w.device)
+    zero = torch.empty_like(scale)
+    _check("w4_quantize_groupwise", lib().w4_quantize_groupwise(
+        _ptr(w), wdt, N, K, group, _ptr(packed), _ptr(scale), _ptr(zero),
+        W4_F32 if sz_dtype == torch.float32 else W4_BF16, _stream(stream)))
+    return packed, scale, zero
+
+
+def w4a16_embedding(ids, w_tiled, sz_tiled, group: int, V: int, K: int, out=None, stream=None):
+    """ids int32 [T] -> bf16 [T, K]: rows of the tiled [V, K] table, dequantized."""
+    T = ids.numel()
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=ids.device)
+    _check("w4a16_embedding", lib().w4a16_embedding(
+        _ptr(ids), T, _ptr(w_tiled), _ptr(sz_tiled), group, V, K, _ptr(out), _stream(stream)))
     return out
 
 

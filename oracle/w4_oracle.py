@@ -203,6 +203,24 @@ def quantize_groupwise(w: np.ndarray, group: int):
     return q.reshape(n, k).astype(np.uint8), scale, zero
 
 
+def quantize_groupwise_f32(w32: np.ndarray, group: int):
+    """[cpu_int4] quantize_groupwise with its own precision: the page converts
+    the weights to float32 (w.float()) and every step is a float32 operation,
+    each rounded to nearest even; torch's round_ is half-to-even. Returns codes
+    uint8 [N, K], scale and zero float32 [N, K/group]."""
+    w = np.asarray(w32, dtype=np.float32)
+    n, k = w.shape
+    if k % group:
+        raise ValueError(f"input dim {k} is not a multiple of group size {group}")
+    wf = w.reshape(n, k // group, group)
+    wmin, wmax = wf.min(axis=-1), wf.max(axis=-1)
+    scale = np.maximum(wmax - wmin, np.float32(1e-9)) / np.float32(15.0)
+    zero = wmin + np.float32(8.0) * scale
+    q = np.clip(np.rint((wf - wmin[..., None]) / scale[..., None]), np.float32(0), np.float32(15))
+    assert scale.dtype == np.float32 and q.dtype == np.float32
+    return q.reshape(n, k).astype(np.uint8), scale, zero
+
+
 def dequantize_groupwise(q, scale, zero, group: int) -> np.ndarray:
     """[cpu_int4] w = (q - 8) * scale + zero, scale/zero per (row, group)."""
     q = np.asarray(q, dtype=np.float64)

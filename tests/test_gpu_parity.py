@@ -346,3 +346,59 @@ def test_w4_linear_dispatch(M, threshold):
     else:
         ref = O.w4a8_reference(d["x"], "bf16", d["qweight"], d["scales"], group, bias_bits=d["bias"])["y"]
     assert_close(to_f64(y), ref, f"w4_linear M={M} threshold={threshold}")
+
+
+# ------------------------------------------------------------------ vocab table: groupwise quantizer and embedding
+
+def _rne_bf16_bits(f32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("N,K,group,wdt,szdt", [
+    (37, 512, 64, "bf16", "f32"), (8, 4096, 128, "f16", "f32"), (16, 1536, 512, "f32", "bf16"), (200, 256, 256, "bf16", "bf16")])
+def test_quantize_groupwise(N, K, group, wdt, szdt):
+    rng = np.random.default_rng(N * 7 + K)
+    w32 = (rng.standard_normal((N, K)) * rng.uniform(0.001, 2.0, (N, 1))).astype(np.float32)
+    w32[0, :group] = 1.5                                   # a constant group
+    print(f"\n[quantize_groupwise] N={N} K={K} g={group} {wdt} -> {szdt}", flush=True)
+    if wdt == "f32":
+        wd, wref = torch.from_numpy(w32).to(DEV), w32
+    else:
+        bits = W.to_half_bits(w32, wdt)
+        wd, wref = dev_half(bits, wdt), O.half_bits_to_f32(bits, wdt)
+    packed, s, z = ops.w4_quantize_groupwise(wd, group, torch.float32 if szdt == "f32" else torch.bfloat16)
+    q, rs, rz = O.quantize_groupwise_f32(wref, group)
+    assert np.array_equal(packed.cpu().numpy(), O.pack_nibble_bytes(q))
+    if szdt == "f32":
+        assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(z.cpu().numpy(), rz)
+    else:
+        assert np.array_equal(s.view(torch.int16).cpu().numpy().view(np.uint16), _rne_bf16_bits(rs))
+        assert np.array_equal(z.view(torch.int16).cpu().numpy().view(np.uint16), _rne_bf16_bits(rz))
+
+
+@pytest.mark.parametrize("V,K,group,T", [(1000, 2048, 64, 37), (136, 1536, 128, 300), (64, 192, 64, 9)])
+def test_embedding_and_tied_head(V, K, group, T):
+    """The gather reads the decode head's tiled buffers: rows dequantized as
+    (q-8)*scale+zero (to bf16), and the head on the same buffers is the
+    W4A16 GEMM; ids outside the table give zero rows."""
+    d = W.w4a16_inputs(4, K, V, group, seed=V + K + T)
+    print(f"\n[embedding] V={V} K={K} g={group} T={T}", flush=True)
+    wt, st = ops.w4a16_repack(torch.from_numpy(d["w"]).to(DEV), dev_half(d["scale"], "bf16"),
+                              dev_half(d["zero"], "bf16"), group)
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, V, T).astype(np.int32)
+    ids[0], ids[-1] = V - 1, 0
+    ids[T // 2] = -1
+    if T > 2:
+        ids[1] = V                                           # outside the table
+    emb = ops.w4a16_embedding(torch.from_numpy(ids).to(DEV), wt, st, group, V, K)
+    table = O.dequantize_groupwise(O.unpack_nibble_bytes(d["w"]), O.bf16_bits_to_f32(d["scale"]),
+                                   O.bf16_bits_to_f32(d["zero"]), group)
+    valid = (ids >= 0) & (ids < V)
+    ref = np.zeros((T, K))
+    ref[valid] = table[ids[valid]]
+    got = to_f64(emb)
+    assert np.all(got[~valid] == 0.0)
+    assert_close(got, ref, f"embedding V={V} K={K}")
+    head = ops.w4a16_gemm(dev_half(d["x"], "bf16"), wt, st, group, V)
+    assert_close(to_f64(head), O.w4a16_reference(d["x"], d["w"], d["scale"], d["zero"], group), "tied head")

@@ -444,3 +444,43 @@ def test_w4a16_gptq_brute_force_per_channel():
                 code = (int(words[kk // 8, n]) >> (4 * (kk % 8))) & 15
                 tot += x[m, kk] * (code - 8) * float(s[0, n])
             assert abs(y[m, n] - tot) <= 1e-12 * max(1.0, abs(tot))
+
+
+# ------------------------------------------------------------------ groupwise quantizer in float32
+
+def test_quantize_groupwise_f32_properties():
+    """The float32 quantizer against what the page fixes: every group's min
+    gets code 0 and its max code 15; the dequantized extremes come back to
+    within float32 rounding; codes agree with the float64 quantizer except
+    where the float64 quotient sits within float32 rounding of a half step."""
+    rng = np.random.default_rng(51)
+    w = (rng.standard_normal((6, 512)) * rng.uniform(0.01, 3.0, (6, 1))).astype(np.float32)
+    w[0, :64] = 0.25                               # constant group: scale from the 1e-9 clamp
+    g = 64
+    q, s, z = O.quantize_groupwise_f32(w, g)
+    assert q.dtype == np.uint8 and s.dtype == np.float32 and z.dtype == np.float32
+    wf = w.reshape(6, -1, g)
+    qf = q.reshape(6, -1, g)
+    imin, imax = wf.argmin(-1), wf.argmax(-1)
+    for r in range(6):
+        for gg in range(wf.shape[1]):
+            assert qf[r, gg, imin[r, gg]] == 0
+            if wf[r, gg].max() > wf[r, gg].min():
+                assert qf[r, gg, imax[r, gg]] == 15
+    assert s[0, 0] == np.float32(np.float32(1e-9) / np.float32(15)) and np.all(q[0, :64] == 0)
+    deq = (q.reshape(6, -1, g).astype(np.float64) - 8) * s[..., None] + z[..., None]
+    assert np.allclose(deq.min(-1), wf.min(-1), rtol=0, atol=4 * np.abs(wf).max() * 2.0 ** -23)
+    assert np.allclose(deq.max(-1), wf.max(-1), rtol=0, atol=4 * np.abs(wf).max() * 2.0 ** -23)
+    q64, s64, _ = O.quantize_groupwise(w.astype(np.float64), g)
+    quot = (wf.astype(np.float64) - wf.min(-1, keepdims=True)) / s64[..., None]
+    near_half = np.abs(quot - np.floor(quot) - 0.5) < 1e-4
+    assert np.array_equal(q.reshape(quot.shape)[~near_half], q64.reshape(quot.shape)[~near_half])
+
+
+def test_quantize_groupwise_f32_worked_example():
+    """A group worked by hand: values 0, 1, ..., 15 scaled by 0.5 give
+    scale 0.5, zero 4.0 and codes 0..15 (every quotient is an exact integer)."""
+    w = (np.arange(64, dtype=np.float32) % 16 * np.float32(0.5)).reshape(1, 64)
+    q, s, z = O.quantize_groupwise_f32(w, 64)
+    assert s[0, 0] == np.float32(0.5) and z[0, 0] == np.float32(4.0)
+    assert np.array_equal(q[0], (np.arange(64) % 16).astype(np.uint8))
