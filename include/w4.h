@@ -64,6 +64,10 @@ extern "C" {
 #define W4_LAYOUT_S4_NK    3  /* int8 [N, K/2]: signed int4 two per byte (two's
                                  complement nibbles, value = nibble); converted with
                                  XOR 0x88 ([w4afp8] _repack_signed_int4_to_uint4b8) */
+#define W4_LAYOUT_I8_NK    4  /* int8 [N, K]: one signed int4 value (-8..7) per byte
+                                 ([ct_w4a8] create_weights: weight_packed is int8
+                                 [output, input]); values outside -8..7 are
+                                 undefined (their low nibble is taken) */
 
 /*
  * Per-token dynamic activation quantization.

@@ -134,7 +134,8 @@ int w4_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch, 
   const char* fn = "w4_repack";
   int rc = check_mnk(fn, 0, N, K);
   if (rc) return rc;
-  if (layout != W4_LAYOUT_GPTQ_KN && layout != W4_LAYOUT_CT_NK && layout != W4_LAYOUT_S4_NK)
+  if (layout != W4_LAYOUT_GPTQ_KN && layout != W4_LAYOUT_CT_NK && layout != W4_LAYOUT_S4_NK &&
+      layout != W4_LAYOUT_I8_NK)
     return fail(W4_ERR_INVALID, "%s: unknown source layout %d", fn, layout);
   if (batch < 0 || batch > 65535) return fail(W4_ERR_INVALID, "%s: batch=%lld out of range", fn, (long long)batch);
   if (batch == 0 || N == 0) return ok();

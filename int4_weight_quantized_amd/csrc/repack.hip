@@ -4,7 +4,9 @@
 // qweight the int8 kernel reads), compressed-tensors weight_packed int32
 // [N, K/8] (zentorch page, packed along the input dim) and signed int4 two
 // per byte [N, K/2] (w4afp8 page, _repack_signed_int4_to_uint4b8: XOR 0x88
-// turns each signed nibble s into the uint4b8 code s + 8).
+// turns each signed nibble s into the uint4b8 code s + 8), and one signed
+// int4 value per int8 byte [N, K] (the compressed-tensors W4A8 int scheme's
+// weight_packed, created as int8 [output, input]).
 //
 // One thread per 32-bit word of the tiled output. The eight codes of an
 // output word come from eight (k, n) positions; each is gathered from the
@@ -13,7 +15,8 @@
 
 namespace w4 {
 
-// layout: 1 GPTQ [K/8, N], 2 CT [N, K/8], 3 signed int4 bytes [N, K/2]
+// layout: 1 GPTQ [K/8, N], 2 CT [N, K/8], 3 signed int4 bytes [N, K/2],
+// 4 int8 [N, K] holding values -8..7
 __device__ __forceinline__ uint32_t code_at(const void* src, int layout, int K, int N, int k, int n) {
   if (k >= K || n >= N) return 8u;     // padding: zero weight
   if (layout == 1) {
@@ -23,6 +26,10 @@ __device__ __forceinline__ uint32_t code_at(const void* src, int layout, int K, 
   if (layout == 2) {
     const uint32_t w = reinterpret_cast<const uint32_t*>(src)[(int64_t)n * (K >> 3) + (k >> 3)];
     return (w >> (4 * (k & 7))) & 0xFu;
+  }
+  if (layout == 4) {
+    const uint8_t v = reinterpret_cast<const uint8_t*>(src)[(int64_t)n * K + k];
+    return (v & 0xFu) ^ 0x8u;          // two's-complement low nibble of v in [-8, 7] -> v + 8
   }
   const uint8_t b = reinterpret_cast<const uint8_t*>(src)[(int64_t)n * (K >> 1) + (k >> 1)];
   const uint32_t s = (k & 1) ? (b >> 4) : (b & 0xFu);
@@ -64,7 +71,7 @@ hipError_t launch_repack(const void* src, int layout, int64_t K, int64_t N, int6
                          void* dst, hipStream_t stream) {
   const int64_t words = (int64_t)(tiled_bytes(K, N) / 4);
   const int KT = (int)((K + kTileK - 1) / kTileK);
-  int64_t src_stride = (layout == 3) ? N * (K / 2) : N * (K / 8) * 4;
+  int64_t src_stride = (layout == 3) ? N * (K / 2) : (layout == 4 ? N * K : N * (K / 8) * 4);
   dim3 block(256), grid((unsigned)((words + 255) / 256), (unsigned)batch);
   hipLaunchKernelGGL(repack_kernel, grid, block, 0, stream,
                      static_cast<const uint8_t*>(src), layout, (int)K, (int)N, src_stride,

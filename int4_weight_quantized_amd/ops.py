@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4.so")
 
 W4_BF16, W4_F16, W4_F32, W4_I8, W4_FP8_E4M3 = 1, 2, 3, 4, 5
-W4_LAYOUT_GPTQ_KN, W4_LAYOUT_CT_NK, W4_LAYOUT_S4_NK = 1, 2, 3
+W4_LAYOUT_GPTQ_KN, W4_LAYOUT_CT_NK, W4_LAYOUT_S4_NK, W4_LAYOUT_I8_NK = 1, 2, 3, 4
 W4_LINEAR_MIN_TOKENS_INT8 = 33          # include/w4.h: the library's default dispatch threshold
 ERRORS = {0: "OK", -1: "INVALID", -2: "ALIGN", -3: "GROUP", -4: "DTYPE", -5: "UNSUPPORTED", -6: "HIP"}
 

@@ -163,6 +163,14 @@ def unpack_ct_nk(w: np.ndarray) -> np.ndarray:
     return _nibbles_of_words(w)
 
 
+def unpack_i8_nk(w: np.ndarray) -> np.ndarray:
+    """[ct_w4a8] create_weights: weight_packed int8 [N, K], one signed int4
+    value per byte -> codes uint8 [N, K] with the zero point 8 (q = v + 8)."""
+    v = np.asarray(w, dtype=np.int16)
+    assert v.min() >= -8 and v.max() <= 7, "int4 values"
+    return (v + 8).astype(np.uint8)
+
+
 def pack_nibble_bytes(q: np.ndarray) -> np.ndarray:
     """[cpu_int4] pack_nibbles: codes [N, K] -> uint8 [N, K/2], byte j holds
     code 2j in its low nibble and code 2j+1 in its high nibble."""

@@ -210,7 +210,7 @@ def test_w4a8_linear_workloads(name):
 
 
 def test_repack_layouts_agree():
-    """compressed-tensors [N,K/8] and signed-int4 bytes give the same tiled weights as GPTQ."""
+    """compressed-tensors [N,K/8], signed-int4 bytes and int8 [N,K] give the same tiled weights as GPTQ."""
     K, N = 384, 264
     d = W.w4a8_inputs(8, K, N, 128, "bf16", seed=5)
     qw = d["qweight"]                                          # GPTQ [K/8, N]
@@ -219,7 +219,10 @@ def test_repack_layouts_agree():
     t_g = ops.w4_repack(torch.from_numpy(qw).to(DEV), ops.W4_LAYOUT_GPTQ_KN, K, N)
     t_c = ops.w4_repack(torch.from_numpy(ct).to(DEV), ops.W4_LAYOUT_CT_NK, K, N)
     t_s = ops.w4_repack(torch.from_numpy(s4).to(DEV), ops.W4_LAYOUT_S4_NK, K, N)
-    assert torch.equal(t_g, t_c) and torch.equal(t_g, t_s)
+    i8 = (O.unpack_gptq_kn(qw).T.astype(np.int16) - 8).astype(np.int8)   # int8 [N, K], values -8..7
+    assert np.array_equal(O.unpack_i8_nk(i8), O.unpack_gptq_kn(qw).T)
+    t_i = ops.w4_repack(torch.from_numpy(np.ascontiguousarray(i8)).to(DEV), ops.W4_LAYOUT_I8_NK, K, N)
+    assert torch.equal(t_g, t_c) and torch.equal(t_g, t_s) and torch.equal(t_g, t_i)
     codes = torch.randint(-127, 128, (8, K), dtype=torch.int8, device=DEV)
     P = ops.w4a8_gemm_partials(codes, t_s, 128, N)
     Pref = O.group_partials(codes.cpu().numpy(), O.unpack_gptq_kn(qw), 128)

@@ -484,3 +484,16 @@ def test_quantize_groupwise_f32_worked_example():
     q, s, z = O.quantize_groupwise_f32(w, 64)
     assert s[0, 0] == np.float32(0.5) and z[0, 0] == np.float32(4.0)
     assert np.array_equal(q[0], (np.arange(64) % 16).astype(np.uint8))
+
+
+def test_unpack_i8_nk_exhaustive():
+    """int8 [N, K] weights: every int4 value -8..7 maps to its uint4b8 code
+    v + 8, the same code the signed-nibble XOR 0x88 repack gives."""
+    v = np.arange(-8, 8, dtype=np.int8).reshape(1, 16)
+    q = O.unpack_i8_nk(v)
+    assert np.array_equal(q[0], np.arange(16, dtype=np.uint8))
+    nib = (v.astype(np.int16) & 0xF).astype(np.uint8)                 # two's-complement nibbles
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)     # two per byte, low first
+    assert np.array_equal(O.unpack_nibble_bytes(packed ^ np.uint8(0x88)), q)
+    with pytest.raises(AssertionError):
+        O.unpack_i8_nk(np.array([[8]], dtype=np.int8))
