@@ -101,6 +101,22 @@ int w4a8_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t 
                       float* group_sums, int64_t group, void* stream);
 
 /*
+ * The same quantization with a static input scale instead of the per-token
+ * one. [ct_w4a8] CompressedTensorsW4A8Int takes is_static_input_scheme: a
+ * calibrated, per-tensor activation scale fixed at load time. Every row uses
+ *   code = clamp(rne(x / s), -127, 127)  (W4_I8; fp32 divide), or
+ *   code = E4M3(x / s) saturating       (W4_FP8_E4M3),
+ * so values beyond the calibrated range saturate.
+ *   static_scale  device, one fp32 (> 0; 0 gives all-zero codes)
+ *   scales        device, [M] fp32 out: static_scale copied to every row, the
+ *                 per-row scale array that w4a8_gemm / w4a8_grouped_gemm read
+ *   other arguments and errors as w4a8_quantize_act.
+ */
+int w4a8_quantize_act_static(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const float* static_scale, void* codes, int code_dtype, float* scales,
+                             float* group_sums, int64_t group, void* stream);
+
+/*
  * Size in bytes of one weight matrix in the kernel-tiled layout produced by
  * w4_repack (tiles of 128 output columns x 128 K, 8 KiB each, ragged edges
  * padded with code 8, i.e. zero weight).

@@ -10,7 +10,8 @@
 
 namespace w4 {
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, void* codes,
-                            bool fp8, float* scales, float* gsums, int group, hipStream_t stream);
+                            bool fp8, float* scales, float* gsums, int group, hipStream_t stream,
+                            const float* static_scale = nullptr);
 size_t tiled_bytes(int64_t K, int64_t N);
 hipError_t launch_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch, void* dst,
                          hipStream_t stream);
@@ -89,9 +90,9 @@ const char* w4_last_error(void) { return g_err; }
 
 int w4_version(void) { return 101; }
 
-int w4a8_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, void* codes,
-                      int code_dtype, float* scales, float* group_sums, int64_t group, void* stream) {
-  const char* fn = "w4a8_quantize_act";
+static int quantize_act(const char* fn, const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, void* codes,
+                        int code_dtype, float* scales, float* group_sums, int64_t group, const float* static_scale,
+                        void* stream) {
   if (M < 0 || K < 0) return fail(W4_ERR_INVALID, "%s: negative size M=%lld K=%lld", fn, (long long)M, (long long)K);
   if (x_dtype != W4_BF16 && x_dtype != W4_F16)
     return fail(W4_ERR_DTYPE, "%s: activations must be bf16 or fp16 (dtype code %d)", fn, x_dtype);
@@ -117,8 +118,22 @@ int w4a8_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t 
   if ((reinterpret_cast<uintptr_t>(codes) & 7u) != 0) return fail(W4_ERR_ALIGN, "%s: codes must be 8-byte aligned", fn);
   return hip_status(w4::launch_quant_act(x, x_dtype == W4_BF16, M, K, ldx, codes, code_dtype == W4_FP8_E4M3,
                                          scales, group_sums, (int)(group_sums ? group : 8),
-                                         static_cast<hipStream_t>(stream)),
+                                         static_cast<hipStream_t>(stream), static_scale),
                     fn);
+}
+
+int w4a8_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, void* codes,
+                      int code_dtype, float* scales, float* group_sums, int64_t group, void* stream) {
+  return quantize_act("w4a8_quantize_act", x, x_dtype, M, K, ldx, codes, code_dtype, scales, group_sums, group,
+                      nullptr, stream);
+}
+
+int w4a8_quantize_act_static(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const float* static_scale, void* codes, int code_dtype, float* scales,
+                             float* group_sums, int64_t group, void* stream) {
+  const char* fn = "w4a8_quantize_act_static";
+  if (!static_scale && M > 0) return fail(W4_ERR_INVALID, "%s: null static scale", fn);
+  return quantize_act(fn, x, x_dtype, M, K, ldx, codes, code_dtype, scales, group_sums, group, static_scale, stream);
 }
 
 int w4_repack_bytes(int64_t K, int64_t N, size_t* bytes) {

@@ -39,7 +39,7 @@ template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kQThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int K,
     uint8_t* __restrict__ codes, float* __restrict__ scales,
-    float* __restrict__ gsums, int group) {
+    float* __restrict__ gsums, int group, const float* __restrict__ static_scale) {
   __shared__ float red[kQThreads / kWave];
   const int m = blockIdx.x;
   const int t = threadIdx.x;
@@ -71,7 +71,8 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
-  const float s = __fdiv_rn(amax, FP8 ? 448.0f : 127.0f);
+  // a static (calibrated, per-tensor) scale replaces the row's own
+  const float s = static_scale ? *static_scale : __fdiv_rn(amax, FP8 ? 448.0f : 127.0f);
   if (t == 0) scales[m] = s;
   const bool zero_row = !(s > 0.f);
   const int gchunks = group >> 3;   // chunks per group (power of two <= 64) for gsums
@@ -142,19 +143,19 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(
 
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
                             void* codes, bool fp8, float* scales, float* gsums, int group,
-                            hipStream_t stream) {
+                            hipStream_t stream, const float* static_scale) {
   if (M == 0) return hipSuccess;
   dim3 grid((unsigned)M), block(kQThreads);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint8_t* cp = static_cast<uint8_t*>(codes);
   if (bf16 && !fp8)
-    hipLaunchKernelGGL((quant_act_kernel<true, false>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, nullptr, 8);
+    hipLaunchKernelGGL((quant_act_kernel<true, false>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, nullptr, 8, static_scale);
   else if (!bf16 && !fp8)
-    hipLaunchKernelGGL((quant_act_kernel<false, false>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, nullptr, 8);
+    hipLaunchKernelGGL((quant_act_kernel<false, false>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, nullptr, 8, static_scale);
   else if (bf16 && fp8)
-    hipLaunchKernelGGL((quant_act_kernel<true, true>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, gsums, group);
+    hipLaunchKernelGGL((quant_act_kernel<true, true>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, gsums, group, static_scale);
   else
-    hipLaunchKernelGGL((quant_act_kernel<false, true>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, gsums, group);
+    hipLaunchKernelGGL((quant_act_kernel<false, true>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, gsums, group, static_scale);
   return hipGetLastError();
 }
 

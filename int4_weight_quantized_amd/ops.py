@@ -24,6 +24,7 @@ _I = ctypes.c_int
 
 _SIGS = {
     "w4a8_quantize_act": [_P, _I, _I64, _I64, _I64, _P, _I, _P, _P, _I64, _P],
+    "w4a8_quantize_act_static": [_P, _I, _I64, _I64, _I64, _P, _P, _I, _P, _P, _I64, _P],
     "w4_repack_bytes": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "w4_repack": [_P, _I, _I64, _I64, _I64, _P, _P],
     "w4a8_gemm": [_P, _P, _P, _P, _I, _I64, _P, _P, _I, _I64, _I64, _I64, _P],
@@ -116,6 +117,22 @@ def quantize_act_into(x, codes, scales, group_sums=None, group=0, fp8=False, str
     _check("w4a8_quantize_act", lib().w4a8_quantize_act(
         _ptr(x), _half_code(x.dtype), M, K, K, _ptr(codes), W4_FP8_E4M3 if fp8 else W4_I8,
         _ptr(scales), _ptr(group_sums), group, _stream(stream)))
+
+
+def w4a8_quantize_act_static(x: torch.Tensor, static_scale: torch.Tensor, code_dtype: str = "i8",
+                             group_sums_group: int | None = None, stream=None):
+    """As w4a8_quantize_act with a calibrated per-tensor scale (device fp32 tensor of one element)."""
+    M, K = x.shape
+    fp8 = code_dtype == "fp8"
+    codes = torch.empty((M, K), dtype=torch.uint8 if fp8 else torch.int8, device=x.device)
+    scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    gs = None
+    if group_sums_group is not None:
+        gs = torch.empty((M, K // group_sums_group), dtype=torch.float32, device=x.device)
+    _check("w4a8_quantize_act_static", lib().w4a8_quantize_act_static(
+        _ptr(x), _half_code(x.dtype), M, K, K, _ptr(static_scale), _ptr(codes), W4_FP8_E4M3 if fp8 else W4_I8,
+        _ptr(scales), _ptr(gs), group_sums_group or 0, _stream(stream)))
+    return codes, scales, gs
 
 
 def w4_repack_bytes(K: int, N: int) -> int:

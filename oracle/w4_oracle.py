@@ -90,6 +90,17 @@ def quantize_act_int8(x32: np.ndarray):
 # --------------------------------------------------------------------------
 
 
+def quantize_act_int8_static(x32: np.ndarray, s) -> np.ndarray:
+    """[ct_w4a8] is_static_input_scheme: one calibrated fp32 scale for every
+    row. READING: code = clamp(rne(fl32(x / s)), -127, 127), the symmetric int8
+    rule of the dynamic path with the row scale replaced; s = 0 gives zeros."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    s = np.float32(s)
+    if not s > 0:
+        return np.zeros(x32.shape, dtype=np.int8)
+    return np.clip(np.rint(x32 / s), -127, 127).astype(np.int8)
+
+
 def e4m3_decode(codes) -> np.ndarray:
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     sign = np.where(c >> 7, -1.0, 1.0)

@@ -405,3 +405,32 @@ def test_embedding_and_tied_head(V, K, group, T):
     assert_close(got, ref, f"embedding V={V} K={K}")
     head = ops.w4a16_gemm(dev_half(d["x"], "bf16"), wt, st, group, V)
     assert_close(to_f64(head), O.w4a16_reference(d["x"], d["w"], d["scale"], d["zero"], group), "tied head")
+
+
+# ------------------------------------------------------------------ static (calibrated) activation scale
+
+@pytest.mark.parametrize("dtype,code", [("bf16", "i8"), ("f16", "i8"), ("bf16", "fp8")])
+def test_static_quant_and_gemm(dtype, code):
+    M, K, N, group = 40, 1024, 264, 128
+    d = W.w4a8_inputs(M, K, N, group, dtype, seed=77, outlier_frac=0.01)
+    x32 = O.half_bits_to_f32(d["x"], dtype)
+    s_static = np.float32(np.abs(x32).max() / 2 / (127.0 if code == "i8" else 448.0))   # half the range: saturates
+    print(f"\n[static quant] {dtype} {code} s={s_static}", flush=True)
+    x = dev_half(d["x"], dtype)
+    sd = torch.tensor([s_static], dtype=torch.float32, device=DEV)
+    codes, scales, gs = ops.w4a8_quantize_act_static(x, sd, code, group_sums_group=128 if code == "fp8" else None)
+    assert np.all(scales.cpu().numpy() == s_static)
+    if code == "i8":
+        rc = O.quantize_act_int8_static(x32, s_static)
+        assert np.array_equal(codes.cpu().numpy(), rc)
+        assert (np.abs(rc) == 127).sum() > 0                      # some saturated
+        wt, sc = _tiled_weights(d)
+        y = ops.w4a8_gemm(codes, scales, wt, sc, group, N, out_dtype=x.dtype)
+        P = O.group_partials(rc, O.unpack_gptq_kn(d["qweight"]), group)
+        ref = O.w4a8_epilogue(P, np.full(M, s_static), np.asarray(d["scales"], dtype=np.float32))
+        assert_close(to_f64(y), ref, f"static W4A8 {dtype}")
+    else:
+        rc = O.e4m3_encode((x32 / s_static).astype(np.float32))
+        assert np.array_equal(codes.cpu().numpy(), rc)
+        dec = O.e4m3_decode(rc).reshape(M, -1, 128)
+        assert np.all(np.abs(gs.cpu().numpy() - dec.sum(-1)) <= 1e-6 * np.abs(dec).sum(-1) + 1e-30)

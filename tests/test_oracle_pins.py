@@ -497,3 +497,17 @@ def test_unpack_i8_nk_exhaustive():
     assert np.array_equal(O.unpack_nibble_bytes(packed ^ np.uint8(0x88)), q)
     with pytest.raises(AssertionError):
         O.unpack_i8_nk(np.array([[8]], dtype=np.int8))
+
+
+def test_static_int8_quantizer():
+    """Static scale: hand-worked ties and saturation; with the row's own
+    dynamic scale it gives the (separately pinned) dynamic codes."""
+    x = np.array([[0.25, 0.75, -0.75, 63.25, -63.75, 500.0, -500.0, 0.0]], dtype=np.float32)
+    c = O.quantize_act_int8_static(x, 0.5)
+    assert c.tolist() == [[0, 2, -2, 126, -128 + 1, 127, -127, 0]]     # 0.5->0, 1.5->2, 126.5->126, -127.5 clamps
+    assert not O.quantize_act_int8_static(x, 0.0).any()
+    rng = np.random.default_rng(61)
+    xr = rng.standard_normal((5, 300)).astype(np.float32)
+    codes, s = O.quantize_act_int8(xr)
+    for m in range(5):
+        assert np.array_equal(O.quantize_act_int8_static(xr[m:m + 1], s[m]), codes[m:m + 1])
