@@ -63,9 +63,12 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
     int32_t* __restrict__ partials, int M, int N, int K, int KT, int tilesM, int tilesN) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
-  const int group_chunks = GC > 0 ? GC : group_chunks_rt;
   constexpr bool kPingPong = (MODE == kModeGroup && GC == 2);
+  // group 128: three A-only stages (B stays in registers); otherwise two A+B stages
+  constexpr int kSS = kPingPong ? kStageA : kStage;     // bytes per stage
+  constexpr int kNS = kPingPong ? 3 : 2;                // stages
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kNS * kSS];
+  const int group_chunks = GC > 0 ? GC : group_chunks_rt;
 
   // ---- tile of this block
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -100,13 +103,27 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // unit (64 wn + 16 j + l%16, l/16); the 64 lanes cover one KiB per block j
   const uint32_t wd_voff = 64u * (uint32_t)(lane & 15) + 16u * (uint32_t)(lane >> 4) + 4096u * (uint32_t)wn;
   v4i pb[kPingPong ? 4 : 2];
+  auto gload_a = [&](int tk, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    const uint32_t ks = (uint32_t)tk * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)   // whole offset in the range-checked VGPR operand
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (32 * wave_u + 8 * i) * kBK), 16,
+          a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
+  };
+  auto gload_bd = [&](int tk) {
+    const uint32_t ws = (uint32_t)tk * kTileBytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pb[j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, wd_voff + 1024u * j, ws, 0);
+  };
   auto gload = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
     const uint32_t ks = (uint32_t)tk * kBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i)   // whole offset in the range-checked VGPR operand
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kStage + (32 * wave_u + 8 * i) * kBK), 16,
+          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (32 * wave_u + 8 * i) * kBK), 16,
           a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
     const uint32_t ws = (uint32_t)tk * kTileBytes;
     if constexpr (kPingPong) {
@@ -216,7 +233,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   auto mfma_rows = [&](auto STc, int c, auto I0c, auto I1c, bool fresh, const v4i (&bf)[4]) {
     constexpr int ST = decltype(STc)::value;
     constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
-    const uint8_t* la = lds + ST * kStage + a_ro[c];
+    const uint8_t* la = lds + ST * kSS + a_ro[c];
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const v4i af = *reinterpret_cast<const v4i*>(la + 16 * kBK * i);
@@ -228,7 +245,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
 
   auto read_a = [&](auto STc, int i, int c) -> v4i {
     constexpr int ST = decltype(STc)::value;
-    return *reinterpret_cast<const v4i*>(lds + ST * kStage + a_ro[c] + 16 * kBK * i);
+    return *reinterpret_cast<const v4i*>(lds + ST * kSS + a_ro[c] + 16 * kBK * i);
   };
   auto mfma_row = [&](int i, const v4i& af, const v4i (&bf)[4], bool fresh) {
 #pragma unroll
@@ -243,17 +260,27 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     }
   };
 
-  // ---- prologue: tile 0 to LDS stage 0
-  gload(0, IC<0>{});
+  // ---- prologue: tile 0 to LDS stage 0 (group 128: tiles 0 and 1 to stages
+  // 0 and 1, and B of tile 0 to registers)
   h2 scr_cur[2] = {h2{0, 0}, h2{0, 0}}, scr_prev[2] = {h2{0, 0}, h2{0, 0}};
-  if constexpr (kPingPong) fetch_scales(0, scr_cur);
-  if constexpr (!kPingPong) lstore_b(IC<0>{});
-  wait_loads();
+  if constexpr (kPingPong) {
+    fetch_scales(0, scr_cur);
+    gload_bd(0);
+    gload_a(0, IC<0>{});
+    gload_a(min(1, KT - 1), IC<1>{});
+    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): all but tile 1's A
+  } else {
+    gload(0, IC<0>{});
+    lstore_b(IC<0>{});
+    wait_loads();
+  }
   __syncthreads();
 
-  // K step tk reads LDS stage ST = tk & 1 while tile tk + 1 streams into the
-  // other stage (A directly, B through registers at the end of the step).
-  // Past the last tile the load repeats it, which keeps the body branch-free.
+  // K step tk reads LDS stage ST while the next tiles stream in: with two
+  // stages tile tk + 1 into the other one (A directly, B through registers
+  // stored at the end of the step); with three (group 128) A of tile tk + 2,
+  // and B of tile tk + 1 into registers. Past the last tile the loads repeat
+  // it, which keeps the body branch-free.
   auto kstep = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
     // direct path: this step's B words (loaded during the previous step)
@@ -270,7 +297,16 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
           b1[j][e] = (int)((uint32_t)pb[j][e] & 0xF0F0F0F0u);
         }
     }
-    gload(min(tk + 1, KT - 1), IC<ST ^ 1>{});
+    h2 scr_next[2];
+    if constexpr (kPingPong) {
+      // loads in this order, A of tile tk + 2 last, so that the step can end
+      // waiting for everything but that: vmcnt(4)
+      fetch_scales(min(tk + 1, G - 1), scr_next);
+      gload_bd(min(tk + 1, KT - 1));
+      gload_a(min(tk + 2, KT - 1), IC<(ST + 2) % 3>{});
+    } else {
+      gload(min(tk + 1, KT - 1), IC<ST ^ 1>{});
+    }
     if constexpr (kPingPong) {
       // Four quarters, each eight MFMAs with four vector ALU ops after each:
       //   Q1  rows 0-1, chunk 0 (fresh)  |  rows 2-3 finish group tk - 1 (row 2)
@@ -278,8 +314,6 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       //   Q3  rows 2-3, chunk 0 (fresh)  |  rows 0-1 finish group tk (row 0)
       //   Q4  rows 2-3, chunk 1          |  (row 1), then B unpack and store
       // At tk = 0 rows 2-3 are still zero, so their epilogue adds nothing.
-      h2 scr_next[2];
-      fetch_scales(min(tk + 1, G - 1), scr_next);
       const v4i a00 = read_a(IC<ST>{}, 0, 0), a10 = read_a(IC<ST>{}, 1, 0);
       const v4i a01 = read_a(IC<ST>{}, 0, 1), a11 = read_a(IC<ST>{}, 1, 1);
       mfma_row(0, a00, b0, true);
@@ -335,16 +369,30 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       }
       lstore_b(IC<ST ^ 1>{});
     }
-    wait_loads();
+    if constexpr (kPingPong)
+      __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): tile tk + 2's A may stay in flight
+    else
+      wait_loads();
     __syncthreads();
   };
 
   int tk = 0;
-  for (; tk + 1 < KT; tk += 2) {
-    kstep(tk, IC<0>{});
-    kstep(tk + 1, IC<1>{});
+  if constexpr (kPingPong) {
+    // stage tk % 3; tile tk + 2 streams in while tk is worked on
+    for (; tk + 2 < KT; tk += 3) {
+      kstep(tk, IC<0>{});
+      kstep(tk + 1, IC<1>{});
+      kstep(tk + 2, IC<2>{});
+    }
+    if (tk < KT) kstep(tk, IC<0>{});
+    if (tk + 1 < KT) kstep(tk + 1, IC<1>{});
+  } else {
+    for (; tk + 1 < KT; tk += 2) {
+      kstep(tk, IC<0>{});
+      kstep(tk + 1, IC<1>{});
+    }
+    if (tk < KT) kstep(tk, IC<0>{});
   }
-  if (tk < KT) kstep(tk, IC<0>{});
   if constexpr (kPingPong) epilogue(IC<2>{}, IC<4>{}, scr_prev, KT - 1);
   if constexpr (MODE == kModePartials) return;
 
@@ -372,7 +420,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) sa[i][r] = a_scale[min(mrow0 + 16 * i + r, M - 1)] * 0.0625f;
   constexpr int kORow = kBN * 2 + 16;                    // padded output row in LDS, bytes
-  static_assert(kBM * kORow <= 2 * kStage, "output tile fits the stage buffers");
+  static_assert(kBM * kORow <= kNS * kSS, "output tile fits the stage buffers");
   const int orow0 = 64 * wm + 4 * (lane >> 4), ocol0 = 64 * wn + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
