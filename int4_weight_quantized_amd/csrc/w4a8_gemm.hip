@@ -22,9 +22,9 @@
 //   into registers, one 16-byte tile unit per lane and column block: lane
 //   (column c, group q) holds the 32 codes of K quarter q of column c, the
 //   low nibbles serve the first 64-deep MFMA step and the high nibbles the
-//   second, and the A fragments are read with the same K assignment (chunk
-//   2q + step). That halves the LDS traffic (3% faster than staging B in
-//   LDS). The other modes unpack B once per block into LDS.
+//   second, and the A fragments carry the same K assignment (chunk 2q +
+//   step, stored where the bank-conflict-free read pattern finds it). That
+//   halves the LDS traffic. The other modes unpack B once per block into LDS.
 // - A and B rows in LDS are 128 bytes; 16-byte chunk kc of row r sits at
 //   kc ^ (r & 7). Fragment reads and tile writes are then bank-conflict free
 //   (measured), and every fragment address is a base register plus an
@@ -97,7 +97,13 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       make_rsrc(reinterpret_cast<const uint8_t*>(Wt) + (int64_t)tn * KT * kTileBytes, (uint32_t)KT * kTileBytes);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lrow = lane >> 3, lchunk = lane & 7;
-  const uint32_t a_voff = (uint32_t)(32 * wave + lrow) * (uint32_t)K + 16u * (uint32_t)(lchunk ^ lrow);
+  // Group 128 (B in registers) reads logical chunk 2q + s for lane group q
+  // and step s; it is stored at physical chunk (4s + q) ^ (row & 7), the
+  // position the two-stage path reads for its own chunk 4s + q, which keeps
+  // the fragment reads bank-conflict free. So the lane at physical chunk p
+  // fetches logical chunk vinv(p ^ (row & 7)), vinv(u) = 2 (u & 3) + (u >> 2).
+  const int a_lchunk = kPingPong ? 2 * ((lchunk ^ lrow) & 3) + ((lchunk ^ lrow) >> 2) : (lchunk ^ lrow);
+  const uint32_t a_voff = (uint32_t)(32 * wave + lrow) * (uint32_t)K + 16u * (uint32_t)a_lchunk;
   const uint32_t w_voff = 16u * tid;                                               // units tid, tid+256
   // direct path: lane (column l%16 of 16-column block j, K quarter l/16) loads
   // unit (64 wn + 16 j + l%16, l/16); the 64 lanes cover one KiB per block j
@@ -218,9 +224,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   const int fl = lane & 7;                                // row & 7 of the lane's fragment rows
   int a_ro[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-    a_ro[c] = (64 * wm + (lane & 15)) * kBK +
-              16 * ((kPingPong ? 2 * (lane >> 4) + c : 4 * c + (lane >> 4)) ^ fl);
+  for (int c = 0; c < 2; ++c) a_ro[c] = (64 * wm + (lane & 15)) * kBK + 16 * ((4 * c + (lane >> 4)) ^ fl);
   int b_ro[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) b_ro[c] = (64 * wn + (lane & 15)) * kBK + 16 * ((4 * c + (lane >> 4)) ^ fl);
