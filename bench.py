@@ -185,6 +185,28 @@ def main():
                                         "first_M_int8_faster": cross}}), flush=True)
         return
 
+    # ------------------------------------------------------------ one GPU's share under tensor parallelism (8)
+    # column shard: N/8 output columns; row shard: K/8 input columns (its
+    # partial outputs would be summed across GPUs, not done here)
+    shards = {}
+    if args.only in ("all", "w4a8"):
+        tp = 8
+        Nc, Kr = N // tp, K // tp
+        wt_c = ops.w4_repack(qw[:, :Nc].contiguous(), ops.W4_LAYOUT_GPTQ_KN, K, Nc)
+        sc_c = sc[:, :Nc].contiguous()
+        y_c = torch.empty((M, Nc), dtype=torch.bfloat16, device=dev)
+        wt_r = ops.w4_repack(qw[: Kr // 8].contiguous(), ops.W4_LAYOUT_GPTQ_KN, Kr, N)
+        sc_r = sc[: Kr // g].contiguous()
+        codes_r = codes[:, :Kr].contiguous()
+        f_c = lambda: ops.w4a8_gemm(codes, s_a, wt_c, sc_c, g, Nc, out=y_c)
+        f_r = lambda: ops.w4a8_gemm(codes_r, s_a, wt_r, sc_r, g, N, out=y)
+        (t_c, t_r), _, _ = timed([f_c, f_r], max(4, args.steps // 2), max(2, args.warmup // 2))
+        for name, t, (mm, nn, kk) in (("column", t_c, (M, Nc, K)), ("row", t_r, (M, N, Kr))):
+            shards[f"tp{tp}_{name}"] = {"M": mm, "N": nn, "K": kk, "gemm_us": t * 1e3,
+                                        "tops": 2.0 * mm * nn * kk / (t * 1e-3) / 1e12,
+                                        "frac_int8_peak": 2.0 * mm * nn * kk / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS}
+        del wt_c, wt_r
+
     # ------------------------------------------------------------ W4A16 decode
     decode = {}
     if args.only in ("all", "decode"):
@@ -288,7 +310,7 @@ def main():
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": w4a8["workload"], "global_batch": M, "seq_len": 1, "parallelism": "single_gpu",
                    "step": "w4a8_quantize_act + w4a8_gemm"},
-        "w4a8": w4a8, "decode": decode, "moe": moe, "vocab": vocab,
+        "w4a8": w4a8, "shards": shards, "decode": decode, "moe": moe, "vocab": vocab,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
