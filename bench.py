@@ -171,7 +171,7 @@ def main():
         for Mc in (1, 2, 4, 8, 16, 24, 32, 48, 64, 80, 96, 112, 128, 192, 256, 384, 512):
             xc = x[:Mc]
             yc = torch.empty((Mc, N), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty((ops.w4_linear_workspace_bytes(Mc, K, 1),), dtype=torch.uint8, device=dev)
+            ws = torch.empty((ops.w4_linear_workspace_bytes(Mc, N, K, g, 1),), dtype=torch.uint8, device=dev)
             f_wo = [(lambda w=w: ops.w4_linear(xc, w, sc, g, N, min_tokens_int8=1 << 30, out=yc)) for w in wts]
             f_i8 = [(lambda w=w: ops.w4_linear(xc, w, sc, g, N, min_tokens_int8=1, out=yc, workspace=ws))
                     for w in wts]

@@ -265,16 +265,20 @@ int w4a16_tiled_gemm(const void* x, int x_dtype, const void* w_tiled, const void
  *   min_tokens_int8  threshold; <= 0 selects W4_LINEAR_MIN_TOKENS_INT8, the
  *             crossover measured on MI355X for these kernels (the page's 512
  *             was measured for its own device)
- *   workspace device scratch of at least w4_linear_workspace_bytes(M, K,
- *             min_tokens_int8) bytes (16-byte aligned; may be NULL when that
- *             is 0): int8 codes and fp32 row scales of the int8 path. The
+ *   workspace device scratch of at least w4_linear_workspace_bytes(M, N, K,
+ *             group, min_tokens_int8) bytes (16-byte aligned; may be NULL
+ *             when that is 0): the int8 path's codes and fp32 row scales and,
+ *             when the GEMM splits K (group 128 with too few tiles to fill
+ *             the chip: few rows), its fp32 partial tiles, summed by a second
+ *             kernel (the sum order is fixed: results are reproducible). The
  *             caller owns it; calls sharing one workspace must not overlap.
  *   x, out    device, 16-byte aligned; out [M, N] in the activation dtype
  *   other arguments as w4a16_tiled_gemm.
  * Errors: those of the path taken, and INVALID when the workspace is too small.
  */
 #define W4_LINEAR_MIN_TOKENS_INT8 33
-int w4_linear_workspace_bytes(int64_t M, int64_t K, int64_t min_tokens_int8, size_t* bytes);
+int w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group, int64_t min_tokens_int8,
+                              size_t* bytes);
 int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_scale, int scale_dtype,
               int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
               int64_t min_tokens_int8, void* workspace, size_t workspace_bytes, void* stream);

@@ -19,6 +19,10 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
                             int64_t group, const void* bias, void* out, bool out_bf16, int32_t* partials,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 void w4a16_tiled_bytes(int64_t K, int64_t N, size_t* wbytes, size_t* szbytes);
+int w4a8_split_count(int64_t M, int64_t N, int64_t K, int64_t group);
+hipError_t launch_w4a8_gemm_split(const int8_t* a, const float* a_scale, const void* w_tiled, const void* w_scale,
+                                  const void* bias, void* out, bool out_bf16, int64_t M, int64_t N, int64_t K,
+                                  int splits, float* ws, hipStream_t stream);
 hipError_t launch_w4a16_repack(const uint8_t* w, const void* scale, const void* zero, int64_t group, int64_t K,
                                int64_t N, void* w_tiled, void* sz_tiled, hipStream_t stream);
 hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled, int64_t group, void* out,
@@ -317,17 +321,31 @@ int w4a16_tiled_gemm(const void* x, int x_dtype, const void* w_tiled, const void
 
 static int64_t linear_threshold(int64_t t) { return t > 0 ? t : W4_LINEAR_MIN_TOKENS_INT8; }
 
-// int8 codes first (rounded up to 256 bytes), then the fp32 row scales
-static size_t linear_workspace(int64_t M, int64_t K, int64_t t) {
-  if (M < linear_threshold(t)) return 0;
-  return (((size_t)M * (size_t)K + 255) & ~(size_t)255) + (size_t)M * 4;
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// int8 codes first, then the fp32 row scales, then (K split) the fp32
+// partial tiles [splits][M][N]; each part starts on a 256-byte boundary
+struct LinearWs {
+  size_t codes, scales, partials, total;
+  int splits;
+};
+static LinearWs linear_workspace(int64_t M, int64_t N, int64_t K, int64_t group, int64_t t) {
+  LinearWs w{0, 0, 0, 0, 1};
+  if (M < linear_threshold(t)) return w;
+  w.splits = w4::w4a8_split_count(M, N, K, group);
+  w.codes = 0;
+  w.scales = round256((size_t)M * (size_t)K);
+  w.partials = w.scales + round256((size_t)M * 4);
+  w.total = w.partials + (w.splits > 1 ? (size_t)w.splits * (size_t)M * (size_t)N * 4 : 0);
+  return w;
 }
 
-int w4_linear_workspace_bytes(int64_t M, int64_t K, int64_t min_tokens_int8, size_t* bytes) {
+int w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group, int64_t min_tokens_int8,
+                              size_t* bytes) {
   const char* fn = "w4_linear_workspace_bytes";
   if (!bytes) return fail(W4_ERR_INVALID, "%s: null output pointer", fn);
-  if (M < 0 || K <= 0) return fail(W4_ERR_INVALID, "%s: sizes must be M >= 0, K > 0", fn);
-  *bytes = linear_workspace(M, K, min_tokens_int8);
+  if (M < 0 || N < 0 || K <= 0) return fail(W4_ERR_INVALID, "%s: sizes must be M >= 0, N >= 0, K > 0", fn);
+  *bytes = linear_workspace(M, N, K, group, min_tokens_int8).total;
   return ok();
 }
 
@@ -340,7 +358,8 @@ int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_sca
   if (M == 0 || N == 0) return ok();
   if (!out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
   if (!aligned16(out) || !aligned16(x)) return fail(W4_ERR_ALIGN, "%s: x and out must be 16-byte aligned", fn);
-  const size_t need = linear_workspace(M, K, min_tokens_int8);
+  const LinearWs lw = linear_workspace(M, N, K, group, min_tokens_int8);
+  const size_t need = lw.total;
   if (workspace_bytes < need || (need && !workspace))
     return fail(W4_ERR_INVALID, "%s: workspace of %zu bytes is smaller than the %zu needed for M=%lld K=%lld", fn,
                 workspace_bytes, need, (long long)M, (long long)K);
@@ -358,10 +377,15 @@ int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_sca
     }
     return ok();
   }
-  int8_t* codes = static_cast<int8_t*>(workspace);
-  float* scales = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + (need - (size_t)M * 4));
+  uint8_t* wsb = static_cast<uint8_t*>(workspace);
+  int8_t* codes = reinterpret_cast<int8_t*>(wsb + lw.codes);
+  float* scales = reinterpret_cast<float*>(wsb + lw.scales);
   rc = hip_status(w4::launch_quant_act(x, !f16, M, K, K, codes, false, scales, nullptr, 0, st), fn);
   if (rc) return rc;
+  if (lw.splits > 1)   // few rows: K split over blocks, fp32 partial tiles summed by a second kernel
+    return hip_status(w4::launch_w4a8_gemm_split(codes, scales, w_tiled, w_scale, bias, out, !f16, M, N, K, lw.splits,
+                                                 reinterpret_cast<float*>(wsb + lw.partials), st),
+                      fn);
   return hip_status(w4::launch_w4a8_gemm(codes, scales, w_tiled, w_scale, group, bias, out, !f16, nullptr, M, N, K, st),
                     fn);
 }

@@ -48,7 +48,10 @@ constexpr int kStageA = kBM * kBK;                 // A rows unpadded, chunks sw
 constexpr int kStageB = kBN * kBK;                 // B rows unpadded, chunks swizzled
 constexpr int kStage = kStageA + kStageB;
 
-enum { kModeGroup = 0, kModeChannel = 1, kModePartials = 2 };
+// kModeSplit: group 128 with K split over `splits` blocks per tile; each
+// writes its fp32 partial tile (a_scale applied, no bias) to ws[split][M][N]
+// and w4a8_split_finalize sums them.
+enum { kModeGroup = 0, kModeChannel = 1, kModePartials = 2, kModeSplit = 3 };
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -62,16 +65,26 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-    int32_t* __restrict__ partials, int M, int N, int K, int KT, int tilesM, int tilesN) {
-  constexpr bool kPingPong = (MODE == kModeGroup && GC == 2);
+    int32_t* __restrict__ partials, int M, int N, int K, int KT, int tilesM, int tilesN,
+    float* __restrict__ ws, int splits) {
+  constexpr bool kPingPong = ((MODE == kModeGroup || MODE == kModeSplit) && GC == 2);
+  static_assert(MODE != kModeSplit || GC == 2, "split K is built for group 128");
   // group 128: three A-only stages (B stays in registers); otherwise two A+B stages
   constexpr int kSS = kPingPong ? kStageA : kStage;     // bytes per stage
   constexpr int kNS = kPingPong ? 3 : 2;                // stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[kNS * kSS];
   const int group_chunks = GC > 0 ? GC : group_chunks_rt;
 
-  // ---- tile of this block
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  // ---- tile of this block (and its K range: all of K unless split)
+  int t = xcd_remap(blockIdx.x, gridDim.x);
+  int kt0 = 0, kt1 = KT, split = 0;
+  if constexpr (MODE == kModeSplit) {
+    const int ks = (KT + splits - 1) / splits;
+    split = t % splits;
+    t /= splits;
+    kt0 = min(split * ks, KT);
+    kt1 = min(kt0 + ks, KT);
+  }
   constexpr int GM = 8;
   const int per_group = GM * tilesN;
   const int first_m = (t / per_group) * GM;
@@ -267,11 +280,21 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // ---- prologue: tile 0 to LDS stage 0 (group 128: tiles 0 and 1 to stages
   // 0 and 1, and B of tile 0 to registers)
   h2 scr_cur[2] = {h2{0, 0}, h2{0, 0}}, scr_prev[2] = {h2{0, 0}, h2{0, 0}};
+  if constexpr (MODE == kModeSplit) {
+    if (kt0 >= kt1) {                              // an empty split (the host avoids them): zeros
+      float* wsp = ws + (int64_t)split * M * N;
+      for (int e = tid; e < kBM * kBN; e += kGThreads) {
+        const int m = m0 + e / kBN, n = n0 + e % kBN;
+        if (m < M && n < N) wsp[(int64_t)m * N + n] = 0.f;
+      }
+      return;
+    }
+  }
   if constexpr (kPingPong) {
-    fetch_scales(0, scr_cur);
-    gload_bd(0);
-    gload_a(0, IC<0>{});
-    gload_a(min(1, KT - 1), IC<1>{});
+    fetch_scales(kt0, scr_cur);
+    gload_bd(kt0);
+    gload_a(kt0, IC<0>{});
+    gload_a(min(kt0 + 1, kt1 - 1), IC<1>{});
     __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): all but tile 1's A
   } else {
     gload(0, IC<0>{});
@@ -305,9 +328,9 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     if constexpr (kPingPong) {
       // loads in this order, A of tile tk + 2 last, so that the step can end
       // waiting for everything but that: vmcnt(4)
-      fetch_scales(min(tk + 1, G - 1), scr_next);
-      gload_bd(min(tk + 1, KT - 1));
-      gload_a(min(tk + 2, KT - 1), IC<(ST + 2) % 3>{});
+      fetch_scales(min(tk + 1, kt1 - 1), scr_next);
+      gload_bd(min(tk + 1, kt1 - 1));
+      gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
     } else {
       gload(min(tk + 1, KT - 1), IC<ST ^ 1>{});
     }
@@ -380,16 +403,16 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     __syncthreads();
   };
 
-  int tk = 0;
+  int tk = kt0;
   if constexpr (kPingPong) {
-    // stage tk % 3; tile tk + 2 streams in while tk is worked on
-    for (; tk + 2 < KT; tk += 3) {
+    // stage (tk - kt0) % 3; tile tk + 2 streams in while tk is worked on
+    for (; tk + 2 < kt1; tk += 3) {
       kstep(tk, IC<0>{});
       kstep(tk + 1, IC<1>{});
       kstep(tk + 2, IC<2>{});
     }
-    if (tk < KT) kstep(tk, IC<0>{});
-    if (tk + 1 < KT) kstep(tk + 1, IC<1>{});
+    if (tk < kt1) kstep(tk, IC<0>{});
+    if (tk + 1 < kt1) kstep(tk + 1, IC<1>{});
   } else {
     for (; tk + 1 < KT; tk += 2) {
       kstep(tk, IC<0>{});
@@ -397,8 +420,25 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     }
     if (tk < KT) kstep(tk, IC<0>{});
   }
-  if constexpr (kPingPong) epilogue(IC<2>{}, IC<4>{}, scr_prev, KT - 1);
+  if constexpr (kPingPong) epilogue(IC<2>{}, IC<4>{}, scr_prev, kt1 - 1);
   if constexpr (MODE == kModePartials) return;
+  if constexpr (MODE == kModeSplit) {
+    // fp32 partial tile with the row scale applied: rows of 16 columns are
+    // 64-byte runs per store instruction
+    float* wsp = ws + (int64_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mrow0 + 16 * i + r;
+        if (m >= M) continue;
+        const float sa = a_scale[m] * 0.0625f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (ncol[j] < N) wsp[(int64_t)m * N + ncol[j]] = facc[i][j][r] * sa;
+      }
+    return;
+  }
 
   if constexpr (MODE == kModeChannel) {
     h2 raw[2];
@@ -463,7 +503,7 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
   const int iM = (int)M, iN = (int)N, iK = (int)K;
 #define W4A8_LAUNCH(MODE_, BF16_, GC_)                                                                  \
   hipLaunchKernelGGL((w4a8_gemm_kernel<MODE_, BF16_, GC_>), grid, block, 0, stream, a, a_scale, W, S, gc, B, O, \
-                     partials, iM, iN, iK, KT, tilesM, tilesN)
+                     partials, iM, iN, iK, KT, tilesM, tilesN, nullptr, 1)
   if (partials) {
     W4A8_LAUNCH(kModePartials, true, 0);
   } else if (group == -1) {
@@ -476,6 +516,84 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
     if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 0); else W4A8_LAUNCH(kModeGroup, false, 0);
   }
 #undef W4A8_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace w4
+
+namespace w4 {
+
+// Splits of K for a group-128 GEMM of this shape: enough blocks to fill the
+// 512 block slots of the chip (two per CU) when the tiles alone fill at most a
+// quarter of them, each split keeping at least 4 K steps. 1 = no split.
+// (Measured on the up-projection weights: 112 tiles (M <= 128) split in 4 run
+// 33 -> 22-33 us; 224 tiles split in 2 ran slower than unsplit, the partial
+// tiles' extra traffic outweighing the fuller chip.)
+int w4a8_split_count(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (group != 128) return 1;
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  if (tiles > 128) return 1;
+  const int64_t KT = (K + kBK - 1) / kBK;
+  int s = 1;
+  while (s < 8 && tiles * s * 2 <= 512 && KT / (s * 2) >= 4) s *= 2;
+  while (s > 1 && (int64_t)(s - 1) * ((KT + s - 1) / s) >= KT) s /= 2;   // no empty split
+  return s;
+}
+
+// out[m,n] = cast(sum_s ws[s][m][n] + bias[n]); 8 outputs per thread
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void split_finalize_kernel(const float* __restrict__ ws, int splits, int64_t MN, int N,
+                                                             const uint16_t* __restrict__ bias,
+                                                             uint16_t* __restrict__ out) {
+  const int64_t e0 = 8 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (e0 >= MN) return;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int s_ = 0; s_ < splits; ++s_) {
+    const v4f a = *reinterpret_cast<const v4f*>(ws + s_ * MN + e0);
+    const v4f b = *reinterpret_cast<const v4f*>(ws + s_ * MN + e0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] += a[i];
+      v[4 + i] += b[i];
+    }
+  }
+  const int n0 = (int)(e0 % N);                      // N % 8 == 0: the 8 outputs share a row
+  v4i pk;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = v[2 * i], hi = v[2 * i + 1];
+    if (bias) {
+      lo += OUT_BF16 ? bf16_to_f32(bias[n0 + 2 * i]) : f16_to_f32(bias[n0 + 2 * i]);
+      hi += OUT_BF16 ? bf16_to_f32(bias[n0 + 2 * i + 1]) : f16_to_f32(bias[n0 + 2 * i + 1]);
+    }
+    const uint32_t l = OUT_BF16 ? f32_to_bf16_rne(lo) : f32_to_f16_rne(lo);
+    const uint32_t h = OUT_BF16 ? f32_to_bf16_rne(hi) : f32_to_f16_rne(hi);
+    pk[i] = (int)(l | (h << 16));
+  }
+  *reinterpret_cast<v4i*>(out + e0) = pk;
+}
+
+hipError_t launch_w4a8_gemm_split(const int8_t* a, const float* a_scale, const void* w_tiled, const void* w_scale,
+                                  const void* bias, void* out, bool out_bf16, int64_t M, int64_t N, int64_t K,
+                                  int splits, float* ws, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int KT = (int)((K + kBK - 1) / kBK);
+  const int tilesM = (int)((M + kBM - 1) / kBM), tilesN = (int)((N + kBN - 1) / kBN);
+  dim3 grid((unsigned)(tilesM * tilesN * splits)), block(kGThreads);
+  hipLaunchKernelGGL((w4a8_gemm_kernel<kModeSplit, true, 2>), grid, block, 0, stream, a, a_scale,
+                     static_cast<const v4i*>(w_tiled), static_cast<const uint16_t*>(w_scale), 2,
+                     static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(nullptr), nullptr, (int)M, (int)N,
+                     (int)K, KT, tilesM, tilesN, ws, splits);
+  const int64_t MN = M * N;
+  dim3 fgrid((unsigned)((MN / 8 + 255) / 256));
+  auto B = static_cast<const uint16_t*>(bias);
+  auto O = static_cast<uint16_t*>(out);
+  if (out_bf16)
+    hipLaunchKernelGGL(split_finalize_kernel<true>, fgrid, dim3(256), 0, stream, ws, splits, MN, (int)N, B, O);
+  else
+    hipLaunchKernelGGL(split_finalize_kernel<false>, fgrid, dim3(256), 0, stream, ws, splits, MN, (int)N, B, O);
   return hipGetLastError();
 }
 

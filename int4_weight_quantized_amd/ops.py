@@ -34,7 +34,7 @@ _SIGS = {
     "w4a16_gemm": [_P, _P, _P, _I64, _P, _I64, _I64, _I64, _P],
     "w4a8_grouped_gemm": [_P, _I, _P, _P, _P, _P, _I64, _P, _P, _I, _I64, _P, _I, _I64, _I64, _I64, _I64, _P],
     "w4a16_tiled_gemm": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _P],
-    "w4_linear_workspace_bytes": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+    "w4_linear_workspace_bytes": [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "w4_linear": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
     "w4_quantize_groupwise": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P],
     "w4a16_embedding": [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P],
@@ -222,9 +222,10 @@ def w4a16_tiled_gemm(x, w_tiled, w_scale, group: int, N: int, bias=None, out=Non
     return out
 
 
-def w4_linear_workspace_bytes(M: int, K: int, min_tokens_int8: int = 0) -> int:
+def w4_linear_workspace_bytes(M: int, N: int, K: int, group: int, min_tokens_int8: int = 0) -> int:
     n = ctypes.c_size_t(0)
-    _check("w4_linear_workspace_bytes", lib().w4_linear_workspace_bytes(M, K, min_tokens_int8, ctypes.byref(n)))
+    _check("w4_linear_workspace_bytes", lib().w4_linear_workspace_bytes(M, N, K, group, min_tokens_int8,
+                                                                        ctypes.byref(n)))
     return n.value
 
 
@@ -235,7 +236,7 @@ def w4_linear(x, w_tiled, w_scale, group: int, N: int, bias=None, min_tokens_int
     M, K = x.shape
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
-    need = w4_linear_workspace_bytes(M, K, min_tokens_int8)
+    need = w4_linear_workspace_bytes(M, N, K, group, min_tokens_int8)
     if workspace is None and need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
     _check("w4_linear", lib().w4_linear(

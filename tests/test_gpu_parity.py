@@ -331,24 +331,30 @@ def test_w4a16_tiled(M, K, N, group, dtype, bias):
     assert_close(to_f64(y), ref, f"w4a16 tiled {M}x{K}x{N} g{group} {dtype}")
 
 
-@pytest.mark.parametrize("M,threshold", [(20, 32), (20, 8), (1, 0), (40, 0)])
-def test_w4_linear_dispatch(M, threshold):
+@pytest.mark.parametrize("M,threshold,group,dtype", [
+    (20, 32, 128, "bf16"), (20, 8, 128, "bf16"), (1, 0, 128, "bf16"), (40, 0, 128, "f16"), (40, 0, 64, "bf16"),
+    (300, 0, 128, "bf16"), (33, 0, -1, "f16")])
+def test_w4_linear_dispatch(M, threshold, group, dtype):
     """Both sides of the per-call dispatch on the same tiled weights: the
     weight-only path (16 rows per launch) below the threshold, per-token int8
-    quantization + W4A8 GEMM from it up."""
-    K, N, group = 1024, 520, 128
-    d = W.w4a8_inputs(M, K, N, group, "bf16", seed=M + 101 * threshold, with_bias=True)
-    print(f"\n[w4_linear] M={M} threshold={threshold}", flush=True)
+    quantization + W4A8 GEMM from it up (group 128 with few tiles splits K:
+    fp32 partial tiles summed by a second kernel)."""
+    K, N = 1024, 520
+    d = W.w4a8_inputs(M, K, N, group, dtype, seed=M + 101 * threshold, with_bias=True)
+    print(f"\n[w4_linear] M={M} threshold={threshold} group={group} {dtype}", flush=True)
     wt, sc = _tiled_weights(d)
-    x = dev_half(d["x"], "bf16")
-    b = dev_half(d["bias"], "bf16")
+    x = dev_half(d["x"], dtype)
+    b = dev_half(d["bias"], dtype)
     y = ops.w4_linear(x, wt, sc, group, N, bias=b, min_tokens_int8=threshold)
+    assert y.dtype == x.dtype
     t = threshold if threshold > 0 else ops.W4_LINEAR_MIN_TOKENS_INT8
     if M < t:
-        ref = O.w4a16_gptq_reference(d["x"], "bf16", d["qweight"], d["scales"], group, bias_bits=d["bias"])
+        ref = O.w4a16_gptq_reference(d["x"], dtype, d["qweight"], d["scales"], group, bias_bits=d["bias"])
     else:
-        ref = O.w4a8_reference(d["x"], "bf16", d["qweight"], d["scales"], group, bias_bits=d["bias"])["y"]
+        ref = O.w4a8_reference(d["x"], dtype, d["qweight"], d["scales"], group, bias_bits=d["bias"])["y"]
     assert_close(to_f64(y), ref, f"w4_linear M={M} threshold={threshold}")
+    y2 = ops.w4_linear(x, wt, sc, group, N, bias=b, min_tokens_int8=threshold)
+    assert torch.equal(y, y2)                                   # reproducible (fixed sum order)
 
 
 # ------------------------------------------------------------------ vocab table: groupwise quantizer and embedding

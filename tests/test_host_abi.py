@@ -110,12 +110,19 @@ def test_repack_bytes(L):
 
 def test_linear_workspace_and_dispatch_checks(L):
     n = ctypes.c_size_t()
-    assert L.w4_linear_workspace_bytes(10, 4096, 0, ctypes.byref(n)) == 0 and n.value == 0   # weight-only
-    assert L.w4_linear_workspace_bytes(64, 4096, 0, ctypes.byref(n)) == 0
-    assert n.value == 64 * 4096 + 64 * 4                                                      # codes + scales
-    assert L.w4_linear_workspace_bytes(100, 200, 0, ctypes.byref(n)) == 0
-    assert n.value == (100 * 200 + 255) // 256 * 256 + 100 * 4
-    assert L.w4_linear_workspace_bytes(64, 4096, 65, ctypes.byref(n)) == 0 and n.value == 0   # own threshold
+    r256 = lambda b: (b + 255) // 256 * 256
+    assert L.w4_linear_workspace_bytes(10, 14336, 4096, 128, 0, ctypes.byref(n)) == 0 and n.value == 0   # weight-only
+    # 64 rows, group 128: 112 tiles -> K split in 4 (fp32 partial tiles after codes and scales)
+    assert L.w4_linear_workspace_bytes(64, 14336, 4096, 128, 0, ctypes.byref(n)) == 0
+    assert n.value == 64 * 4096 + r256(64 * 4) + 4 * 64 * 14336 * 4
+    # group 64 never splits; 4096 rows fill the chip
+    assert L.w4_linear_workspace_bytes(64, 14336, 4096, 64, 0, ctypes.byref(n)) == 0
+    assert n.value == 64 * 4096 + r256(64 * 4)
+    assert L.w4_linear_workspace_bytes(4096, 14336, 4096, 128, 0, ctypes.byref(n)) == 0
+    assert n.value == 4096 * 4096 + r256(4096 * 4)
+    assert L.w4_linear_workspace_bytes(100, 200, 256, 128, 0, ctypes.byref(n)) == 0   # K = 2 steps: no split
+    assert n.value == r256(100 * 256) + r256(100 * 4)
+    assert L.w4_linear_workspace_bytes(64, 14336, 4096, 128, 65, ctypes.byref(n)) == 0 and n.value == 0
     p = ctypes.c_void_p
     # too small a workspace for the int8 path is refused before any launch
     rc = L.w4_linear(p(256), 1, p(256), p(256), 2, 128, None, p(256), 64, 256, 4096, 0, None, 0, None)
