@@ -1,0 +1,70 @@
+// Host driver for the sanitizer build of the C ABI: every call below fails
+// validation (or is an empty no-op), so nothing reaches a GPU. AddressSanitizer
+// and UndefinedBehaviorSanitizer watch the validation code, the error-message
+// formatting (including messages longer than its buffer) and the workspace
+// arithmetic.
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/w4.h"
+
+static int failures = 0;
+static void expect(int got, int want, const char* what) {
+  if (got != want) {
+    std::printf("FAIL %s: got %d want %d (%s)\n", what, got, want, w4_last_error());
+    ++failures;
+  }
+}
+
+int main() {
+  void* p = reinterpret_cast<void*>(256);
+  void* odd = reinterpret_cast<void*>(258);
+  size_t n = 0, wb = 0, sb = 0;
+  expect(w4_version() >= 100, 1, "version");
+  // quantizer
+  expect(w4a8_quantize_act(nullptr, W4_BF16, -1, 256, 256, nullptr, W4_I8, nullptr, nullptr, 0, nullptr), W4_ERR_INVALID, "q neg");
+  expect(w4a8_quantize_act(p, 9, 4, 256, 256, p, W4_I8, (float*)p, nullptr, 0, nullptr), W4_ERR_DTYPE, "q dtype");
+  expect(w4a8_quantize_act(p, W4_BF16, 4, 250, 256, p, W4_I8, (float*)p, nullptr, 0, nullptr), W4_ERR_ALIGN, "q K");
+  expect(w4a8_quantize_act(p, W4_BF16, 4, 256, 128, p, W4_I8, (float*)p, nullptr, 0, nullptr), W4_ERR_ALIGN, "q ldx");
+  expect(w4a8_quantize_act(p, W4_BF16, 4, 256, 256, p, W4_I8, (float*)p, (float*)p, 128, nullptr), W4_ERR_DTYPE, "q gsum i8");
+  expect(w4a8_quantize_act(p, W4_BF16, 4, 256, 256, p, W4_FP8_E4M3, (float*)p, (float*)p, 96, nullptr), W4_ERR_GROUP, "q group");
+  expect(w4a8_quantize_act(odd, W4_BF16, 4, 256, 256, p, W4_I8, (float*)p, nullptr, 0, nullptr), W4_ERR_ALIGN, "q align");
+  expect(w4a8_quantize_act(nullptr, W4_BF16, 0, 256, 256, nullptr, W4_I8, nullptr, nullptr, 0, nullptr), W4_OK, "q empty");
+  expect(w4a8_quantize_act_static(p, W4_BF16, 4, 256, 256, nullptr, p, W4_I8, (float*)p, nullptr, 0, nullptr), W4_ERR_INVALID, "qs null");
+  // repack
+  expect(w4_repack_bytes(100, 24, &n), W4_ERR_ALIGN, "rb align");
+  expect(w4_repack_bytes(256, 24, nullptr), W4_ERR_INVALID, "rb null");
+  expect(w4_repack(p, 7, 256, 256, 1, p, nullptr), W4_ERR_INVALID, "r layout");
+  expect(w4_repack(p, W4_LAYOUT_I8_NK, 256, 256, 1, odd, nullptr), W4_ERR_ALIGN, "r align");
+  expect(w4_repack(p, W4_LAYOUT_GPTQ_KN, 256, 256, 70000, p, nullptr), W4_ERR_INVALID, "r batch");
+  // GEMMs
+  expect(w4a8_gemm((const int8_t*)p, (const float*)p, p, p, W4_BF16, 128, nullptr, p, W4_BF16, 4, 256, 256, nullptr), W4_ERR_DTYPE, "g sdt");
+  expect(w4a8_gemm((const int8_t*)p, (const float*)p, p, p, W4_F16, 96, nullptr, p, W4_BF16, 4, 256, 288, nullptr), W4_ERR_GROUP, "g group");
+  expect(w4a8_gemm((const int8_t*)p, (const float*)p, p, p, W4_F16, 128, nullptr, odd, W4_BF16, 4, 256, 256, nullptr), W4_ERR_ALIGN, "g out");
+  expect(w4a8_gemm((const int8_t*)p, (const float*)p, p, p, W4_F16, 128, nullptr, p, W4_BF16, 4, 260, 256, nullptr), W4_ERR_ALIGN, "g N");
+  expect(w4a8_gemm_partials(nullptr, nullptr, 128, nullptr, 4, 256, 256, nullptr), W4_ERR_INVALID, "gp null");
+  expect(w4a16_repack_bytes(4096, 14336, 48, &wb, &sb), W4_ERR_GROUP, "w16 rb group");
+  expect(w4a16_repack_bytes(1 << 20, 1 << 14, 64, &wb, &sb), W4_ERR_UNSUPPORTED, "w16 rb big");
+  expect(w4a16_gemm(p, p, p, 64, p, 17, 256, 256, nullptr), W4_ERR_UNSUPPORTED, "w16 M");
+  expect(w4a16_repack(nullptr, nullptr, nullptr, W4_F16, 64, 256, 256, nullptr, nullptr, nullptr), W4_ERR_DTYPE, "w16r dt");
+  expect(w4a8_grouped_gemm(p, W4_FP8_E4M3, (const float*)p, (const float*)p, (const int32_t*)p, (const int32_t*)p, 4, p, p,
+                           W4_F16, 128, p, W4_BF16, 1 << 20, 64, 256, 4096, nullptr), W4_ERR_UNSUPPORTED, "grp T*K");
+  expect(w4a8_grouped_gemm(p, W4_I8, (const float*)p, (const float*)p, (const int32_t*)p, (const int32_t*)p, 4, p, p,
+                           W4_F16, 128, p, W4_BF16, 8, 64, 256, 4096, nullptr), W4_ERR_DTYPE, "grp dt");
+  // weight-only, dispatch, vocab table
+  expect(w4a16_tiled_gemm(p, W4_BF16, p, p, W4_F16, 128, nullptr, p, 17, 256, 4096, nullptr), W4_ERR_UNSUPPORTED, "t M");
+  expect(w4_linear_workspace_bytes(64, 14336, 4096, 128, 0, &n), W4_OK, "lw");
+  expect(n == (size_t)64 * 4096 + 256 + (size_t)4 * 64 * 14336 * 4, 1, "lw size");
+  expect(w4_linear(p, W4_BF16, p, p, W4_F16, 128, nullptr, p, 64, 14336, 4096, 0, nullptr, 0, nullptr), W4_ERR_INVALID, "l ws");
+  expect(w4_linear(p, W4_BF16, p, p, W4_F16, 128, nullptr, odd, 4, 256, 4096, 0, nullptr, 0, nullptr), W4_ERR_ALIGN, "l out");
+  expect(w4_quantize_groupwise(p, W4_BF16, 4, 256, 96, (uint8_t*)p, p, p, W4_F32, nullptr), W4_ERR_GROUP, "qg group");
+  expect(w4_quantize_groupwise(p, W4_I8, 4, 256, 64, (uint8_t*)p, p, p, W4_F32, nullptr), W4_ERR_DTYPE, "qg dt");
+  expect(w4a16_embedding(nullptr, 4, p, p, 64, 100, 256, p, nullptr), W4_ERR_ALIGN, "emb V");
+  expect(w4a16_embedding(nullptr, 4, p, p, 64, 128, 256, p, nullptr), W4_ERR_INVALID, "emb null");
+  // the longest message paths: every argument named, sizes at their widest
+  expect(w4a8_gemm((const int8_t*)p, (const float*)p, p, p, W4_F16, 128, nullptr, p, W4_BF16, 4,
+                   (int64_t)1 << 62 | 4, ((int64_t)1 << 62) | 12, nullptr), W4_ERR_UNSUPPORTED, "g huge");
+  if (std::strlen(w4_last_error()) >= 512) { std::printf("FAIL message length\n"); ++failures; }
+  return failures ? 1 : 0;
+}
