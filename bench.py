@@ -231,6 +231,26 @@ def main():
                                 "frac_hbm": nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
             del sets
 
+    # ------------------------------------------------------------ W4A16 prefill: dequantize once + bf16 GEMM
+    prefill = {}
+    if args.only in ("all", "decode"):
+        dd = W.named("w4a16_decode", M=1)
+        Kp, Np, gp, Mp = dd["K"], dd["N"], dd["group"], 4096
+        wb = torch.from_numpy(dd["w"]).to(dev)
+        sp, zp = dev_half(dd["scale"], "bf16"), dev_half(dd["zero"], "bf16")
+        xp = torch.randn((Mp, Kp), dtype=torch.float32, device=dev).to(torch.bfloat16)
+        wdq = torch.empty((Np, Kp), dtype=torch.bfloat16, device=dev)
+        yp = torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)
+        f_dq = lambda: ops.w4a16_dequantize(wb, sp, zp, gp, out=wdq)
+        f_mm = lambda: torch.matmul(xp, wdq.t(), out=yp)
+        (t_dq, t_mm), t_pf, _ = timed([f_dq, f_mm], max(4, args.steps // 5), max(2, args.warmup // 2))
+        dq_bytes = Np * Kp // 2 + 2 * 2 * Np * (Kp // gp) + 2 * Np * Kp
+        prefill = {"workload": f"w4a16 prefill M={Mp} K={Kp} N={Np} group={gp} bf16 (dequantize + bf16 GEMM)",
+                   "dequantize_us": t_dq * 1e3, "dequantize_gbs": dq_bytes / (t_dq * 1e-3) / 1e9,
+                   "gemm_us": t_mm * 1e3, "step_us": t_pf * 1e3,
+                   "step_tflops": 2.0 * Mp * Np * Kp / (t_pf * 1e-3) / 1e12}
+        del wdq, yp
+
     # ------------------------------------------------------------ MoE grouped
     moe = {}
     if args.only in ("all", "moe"):
@@ -310,7 +330,7 @@ def main():
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": w4a8["workload"], "global_batch": M, "seq_len": 1, "parallelism": "single_gpu",
                    "step": "w4a8_quantize_act + w4a8_gemm"},
-        "w4a8": w4a8, "shards": shards, "decode": decode, "moe": moe, "vocab": vocab,
+        "w4a8": w4a8, "shards": shards, "decode": decode, "prefill": prefill, "moe": moe, "vocab": vocab,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -284,6 +284,24 @@ int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_sca
               int64_t min_tokens_int8, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill path of the W4A16 layer: the weight unpacked to bf16 once per call
+ * for an ordinary bf16 GEMM. [cpu_int4] module docstring: large batches
+ * unpack the weight to bf16 once per call and hand it to the ordinary GEMM
+ * (one extra pass over the weights, reading a row-major copy); dequantize:
+ * w = (q - 8) * scale + zero.
+ *   w        device, uint8 [N, K/2], byte j = q[2j] | q[2j+1] << 4 (8-byte aligned)
+ *   scale    device, bf16 [N, K/group]; zero: device bf16 [N, K/group] or NULL
+ *   group    64, 128, 256 or 512, dividing K
+ *   out      device, bf16 [N, K] row-major (16-byte aligned): computed in
+ *            fp32 as fma(q - 8, scale, zero), rounded to nearest even
+ * The GEMM itself (x [M, K] times out^T) is the platform's ordinary bf16 GEMM
+ * (hipBLASLt), not part of this library.
+ * Errors: INVALID, ALIGN, GROUP, DTYPE, UNSUPPORTED (N*K >= 2^31), HIP.
+ */
+int w4a16_dequantize(const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group,
+                     int64_t K, int64_t N, void* out, void* stream);
+
+/*
  * Groupwise min/max int4 quantization of a weight matrix, on the device.
  * [cpu_int4] quantize_groupwise: per row n and group g of `group` columns, in
  * fp32: scale = max(max - min, 1e-9) / 15, zero = min + 8 * scale,

@@ -31,6 +31,8 @@ hipError_t launch_w4a16_tiled(const void* x, bool f16, const void* w_tiled, cons
                               const void* bias, void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_quantize_groupwise(const void* w, int w_dtype_code, int64_t N, int64_t K, int64_t group,
                                      void* packed, void* scale, void* zero, bool sz_bf16, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t* w, const void* scale, const void* zero, int64_t group, int64_t N,
+                             int64_t K, void* out, hipStream_t stream);
 hipError_t launch_embedding(const int32_t* ids, int64_t T, const void* w_tiled, const void* sz_tiled, int64_t group,
                             int64_t V, int64_t K, void* out, hipStream_t stream);
 hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* gsum, const int32_t* row_token,
@@ -425,6 +427,19 @@ int w4a16_embedding(const int32_t* ids, int64_t T, const void* w_tiled, const vo
     return fail(W4_ERR_ALIGN, "%s: w_tiled, sz_tiled and out must be 16-byte aligned", fn);
   return hip_status(w4::launch_embedding(ids, T, w_tiled, sz_tiled, group, V, K, out, static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int w4a16_dequantize(const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group, int64_t K,
+                     int64_t N, void* out, void* stream) {
+  const char* fn = "w4a16_dequantize";
+  if (sz_dtype != W4_BF16) return fail(W4_ERR_DTYPE, "%s: scale and zero must be bf16 (dtype code %d)", fn, sz_dtype);
+  int rc = check_w4a16(fn, group, N, K);
+  if (rc) return rc;
+  if (N == 0) return ok();
+  if (!w || !scale || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if ((reinterpret_cast<uintptr_t>(w) & 7u) || !aligned16(out))
+    return fail(W4_ERR_ALIGN, "%s: w must be 8-byte and out 16-byte aligned", fn);
+  return hip_status(w4::launch_dequantize(w, scale, zero, group, N, K, out, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

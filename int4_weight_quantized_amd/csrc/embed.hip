@@ -173,3 +173,50 @@ hipError_t launch_embedding(const int32_t* ids, int64_t T, const void* w_tiled, 
 }
 
 }  // namespace w4
+
+// ---------------------------------------------------------------- prefill dequantization
+namespace w4 {
+
+// cpu_int4 page (module docstring, dequantize): for many rows the weight is
+// unpacked to bf16 once per call, w = (q - 8) * scale + zero in fp32, and
+// handed to an ordinary GEMM. Reads the row-major byte layout [N, K/2]
+// (byte j = q[2j] | q[2j+1] << 4) with bf16 scale / zero [N, K/group]; one
+// thread per 16 codes (8 bytes in, 32 bytes out; group >= 64 keeps them in
+// one group).
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ scale,
+                                                         const uint16_t* __restrict__ zero, int group, int N, int K,
+                                                         uint16_t* __restrict__ out) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = K / 16;
+  if (id >= (int64_t)N * per_row) return;
+  const int n = (int)(id / per_row), k0 = 16 * (int)(id % per_row);
+  const v2i b = *reinterpret_cast<const v2i*>(w + (int64_t)n * (K / 2) + k0 / 2);
+  const int64_t gi = (int64_t)n * (K / group) + k0 / group;
+  const float s = bf16_to_f32(scale[gi]), z = zero ? bf16_to_f32(zero[gi]) : 0.f;
+  v4i o[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t word = (uint32_t)b[h];            // codes k0 + 8h .. + 7, low nibble first
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = fmaf((float)((word >> (8 * e)) & 15u) - 8.0f, s, z);
+      const float hi = fmaf((float)((word >> (8 * e + 4)) & 15u) - 8.0f, s, z);
+      o[h][e] = (int)((uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16));
+    }
+  }
+  uint16_t* op = out + (int64_t)n * K + k0;
+  *reinterpret_cast<v4i*>(op) = o[0];
+  *reinterpret_cast<v4i*>(op + 8) = o[1];
+}
+
+hipError_t launch_dequantize(const uint8_t* w, const void* scale, const void* zero, int64_t group, int64_t N,
+                             int64_t K, void* out, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int64_t total = N * (K / 16);
+  hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, w,
+                     static_cast<const uint16_t*>(scale), static_cast<const uint16_t*>(zero), (int)group, (int)N,
+                     (int)K, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace w4

@@ -36,6 +36,7 @@ _SIGS = {
     "w4a16_tiled_gemm": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _P],
     "w4_linear_workspace_bytes": [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "w4_linear": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
+    "w4a16_dequantize": [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
     "w4_quantize_groupwise": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P],
     "w4a16_embedding": [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P],
     "w4_last_error": [],
@@ -243,6 +244,16 @@ def w4_linear(x, w_tiled, w_scale, group: int, N: int, bias=None, min_tokens_int
         _ptr(x), _half_code(x.dtype), _ptr(w_tiled), _ptr(w_scale), W4_F16 if w_scale.dtype == torch.float16 else W4_BF16,
         group, _ptr(bias), _ptr(out), M, N, K, min_tokens_int8, _ptr(workspace) if need else None,
         workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def w4a16_dequantize(w, scale, zero, group: int, out=None, stream=None):
+    """Row-major int4 bytes [N, K/2] with bf16 scale/zero [N, K/group] -> bf16 weights [N, K]."""
+    N, K = w.shape[0], w.shape[1] * 2
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    _check("w4a16_dequantize", lib().w4a16_dequantize(
+        _ptr(w), _ptr(scale), _ptr(zero), _half_code(scale.dtype), group, K, N, _ptr(out), _stream(stream)))
     return out
 
 

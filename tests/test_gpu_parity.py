@@ -440,3 +440,39 @@ def test_static_quant_and_gemm(dtype, code):
         assert np.array_equal(codes.cpu().numpy(), rc)
         dec = O.e4m3_decode(rc).reshape(M, -1, 128)
         assert np.all(np.abs(gs.cpu().numpy() - dec.sum(-1)) <= 1e-6 * np.abs(dec).sum(-1) + 1e-30)
+
+
+# ------------------------------------------------------------------ prefill: dequantize once, ordinary GEMM
+
+@pytest.mark.parametrize("N,K,group,zero", [(136, 192, 64, True), (1000, 4096, 128, False), (264, 1536, 512, True)])
+def test_w4a16_dequantize(N, K, group, zero):
+    d = W.w4a16_inputs(4, K, N, group, seed=N + K + group)
+    print(f"\n[dequantize] N={N} K={K} g={group} zero={zero}", flush=True)
+    z = dev_half(d["zero"], "bf16") if zero else None
+    wd = ops.w4a16_dequantize(torch.from_numpy(d["w"]).to(DEV), dev_half(d["scale"], "bf16"), z, group)
+    zb = d["zero"] if zero else np.zeros_like(d["zero"])
+    ref = O.dequantize_groupwise(O.unpack_nibble_bytes(d["w"]), O.bf16_bits_to_f32(d["scale"]),
+                                 O.bf16_bits_to_f32(zb), group)
+    got = to_f64(wd)
+    # one fp32 fma (2^-24 relative) then bf16 rounding: half a bf16 step, at
+    # most 2^-8 of the value (8 significant bits)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -20) + 1e-38)
+
+
+@pytest.mark.parametrize("M,N,K,group", [(64, 1000, 4096, 64), (300, 264, 1536, 128)])
+def test_w4a16_prefill_path(M, N, K, group):
+    """Dequantize once, then the platform's bf16 GEMM (F.linear, hipBLASLt).
+    Bound: each dequantized weight is off by at most 2^-8 of itself (bf16,
+    8 significant bits), the bf16 output by 2^-8 of itself, plus fp32
+    accumulation, so |y - y64| <= 2^-7 * sum_k |x w| + 2^-7 |y64| + 1e-3."""
+    d = W.w4a16_inputs(M, K, N, group, seed=M + N)
+    print(f"\n[prefill] M={M} N={N} K={K} g={group}", flush=True)
+    wd = ops.w4a16_dequantize(torch.from_numpy(d["w"]).to(DEV), dev_half(d["scale"], "bf16"),
+                              dev_half(d["zero"], "bf16"), group)
+    y = torch.nn.functional.linear(dev_half(d["x"], "bf16"), wd)
+    ref = O.w4a16_reference(d["x"], d["w"], d["scale"], d["zero"], group)
+    x = O.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    wabs = np.abs(O.dequantize_groupwise(O.unpack_nibble_bytes(d["w"]), O.bf16_bits_to_f32(d["scale"]),
+                                         O.bf16_bits_to_f32(d["zero"]), group))
+    bound = 2.0 ** -7 * (np.abs(x) @ wabs.T) + 2.0 ** -7 * np.abs(ref) + 1e-3
+    assert np.all(np.abs(to_f64(y) - ref) <= bound)

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for must in ("w4a8_quantize_act", "w4a8_gemm", "w4a16_gemm", "w4a16_repack", "w4a8_grouped_gemm", "w4_repack",
                  "w4_repack_bytes", "w4a8_gemm_partials", "w4a16_tiled_gemm", "w4_linear", "w4_linear_workspace_bytes",
-                 "w4_quantize_groupwise", "w4a16_embedding", "w4a8_quantize_act_static",
+                 "w4_quantize_groupwise", "w4a16_embedding", "w4a8_quantize_act_static", "w4a16_dequantize",
                  "w4_last_error", "w4_version"):
         assert must in names
 
