@@ -42,7 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--only", choices=["all", "w4a8", "decode", "moe", "vocab"], default="all")
+    p.add_argument("--only", choices=["all", "w4a8", "decode", "moe", "vocab", "shards"], default="all",
+                   help="which extra measurements to add to the W4A8 step (shards: only when asked for)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     p.add_argument("--crossover", action="store_true",
                    help="time both paths of w4_linear over a range of row counts on the up-projection "
@@ -189,7 +190,7 @@ def main():
     # column shard: N/8 output columns; row shard: K/8 input columns (its
     # partial outputs would be summed across GPUs, not done here)
     shards = {}
-    if args.only in ("all", "w4a8"):
+    if args.only == "shards":
         tp = 8
         Nc, Kr = N // tp, K // tp
         wt_c = ops.w4_repack(qw[:, :Nc].contiguous(), ops.W4_LAYOUT_GPTQ_KN, K, Nc)
