@@ -5,19 +5,32 @@
 // run time; per the w4afp8 page (W4AFP8Config input_quant) routed-expert
 // activations are quantized per token to 8-bit float, symmetric, dynamic.
 //
-// One 256-thread block per row. The row is read once into registers
-// (16-byte loads, 8 elements per thread per pass), its absmax reduced with
-// wave shuffles and LDS, then every element divided by the scale with
-// correctly rounded fp32 division and rounded: rne + clamp to [-127, 127]
-// for int8, hardware RNE conversion to E4M3 (after clamping to +-448, so it
+// One block per row. Every thread issues all its bounds-checked 16-byte
+// loads (8 elements each, zero past the row end) before using any; the
+// absmax is reduced with wave shuffles and LDS; then every element is
+// divided by the scale and rounded: rne + clamp to [-127, 127] for int8;
+// clamp to +-448, then the hardware RNE conversion to E4M3 (so it
 // saturates) for FP8. Rows longer than the register cache are re-read.
+//
+// The division must be correctly rounded fp32, as the decision is taken on
+// that quotient. For scales in [2^-90, 2^90], x is first clamped to +-b, past
+// which the code is the saturated one anyway (b = 127.25 s for int8, 449 s
+// for FP8), then divided by the usual reciprocal refinement: one Newton step
+// on the hardware reciprocal, once per row, then two fma corrections of the
+// quotient by its remainder. That is exact whenever the remainders are
+// representable, which holds for |x| >= 2^-102, i.e. for every quotient
+// above 2^-12; smaller ones round to a zero code whose sign comes from x.
+// Other scales take the library division.
+//
 // HBM-bound: 2 bytes in + 1 byte out per element.
 #include "w4_device.h"
 
 namespace w4 {
 
-constexpr int kQThreads = 256;
-constexpr int kQCache = 8;   // passes held in registers: K <= 8 * 8 * 256 = 16384
+constexpr int kQThreads = 256;                       // one block per row
+constexpr int kQWaves = kQThreads / kWave;
+constexpr int kQCache = 8;                           // passes held in registers: rows of up to 16384 elements
+constexpr uint32_t kDropped = 0x80000000u;           // buffer offset past any row: the store is dropped
 
 template <bool BF16>
 __device__ __forceinline__ void unpack8(const v4i raw, float (&f)[8]) {
@@ -34,128 +47,197 @@ __device__ __forceinline__ void unpack8(const v4i raw, float (&f)[8]) {
   }
 }
 
-// FP8 = false: int8 codes; true: E4M3 codes (+ optional group sums).
+template <bool BF16>
+__device__ __forceinline__ float absmax8(const v4i raw) {
+  float f[8];
+  unpack8<BF16>(raw, f);
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+  return a;
+}
+
+// Per-row constants of the conversion.
+struct RowScale {
+  float s;          // the row's scale
+  float y;          // 1/s: hardware reciprocal refined by one Newton step
+  float b;          // |x| beyond b decides the saturated code: x is clamped to [-b, b] first
+  bool fast;        // s in [2^-90, 2^90]: divide with div_rn_row
+  bool zero_row;    // s is 0 (or not a positive number): codes are 0
+};
+
+template <bool FP8>
+__device__ __forceinline__ RowScale row_scale(float amax, const float* static_scale) {
+  RowScale r;
+  // a static (calibrated, per-tensor) scale replaces the row's own
+  const float s = static_scale ? *static_scale : __fdiv_rn(amax, FP8 ? 448.0f : 127.0f);
+  r.s = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s)));   // uniform over the wave
+  const float y0 = __builtin_amdgcn_rcpf(r.s);
+  r.y = fmaf(fmaf(-r.s, y0, 1.0f), y0, y0);
+  // int8: |x/s| <= 127.25 rounds to at most 127 and beyond it the code is
+  // +-127; FP8: quotients past 449 clamp to 448 like the quotient of b
+  r.b = (FP8 ? 449.0f : 127.25f) * r.s;
+  r.fast = r.s >= 0x1p-90f && r.s <= 0x1p90f;
+  r.zero_row = !(r.s > 0.f);
+  return r;
+}
+
+// x / r.s correctly rounded for r.fast rows and |x| <= r.b (a zero quotient
+// may lose its sign).
+__device__ __forceinline__ float div_rn_row(float x, const RowScale& r) {
+  const float q0 = x * r.y;
+  const float r0 = fmaf(-r.s, q0, x);
+  const float q1 = fmaf(r0, r.y, q0);
+  const float r1 = fmaf(-r.s, q1, x);
+  return fmaf(r1, r.y, q1);
+}
+
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
+
+__device__ __forceinline__ v2i pack_fp8(const float (&v)[8]) {
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
+  return v2i{w0, w1};
+}
+
+// Low bytes of four words, in order, as one word.
+__device__ __forceinline__ uint32_t low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_amdgcn_perm(b, a, 0x0C0C0400u) | __builtin_amdgcn_perm(d, c, 0x04000C0Cu);
+}
+
+// Codes of one 8-element chunk; for FP8 also returns the sum of the decoded
+// codes (in chunk order) when GSUM.
+template <bool BF16, bool FP8, bool GSUM>
+__device__ __forceinline__ float quantize_chunk(const v4i raw, const RowScale& r, v2i& out) {
+  float f[8], v[8];
+  unpack8<BF16>(raw, f);
+  if (r.fast) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = div_rn_row(__builtin_amdgcn_fmed3f(f[i], -r.b, r.b), r);
+      if (FP8) v[i] = __builtin_copysignf(v[i], f[i]);   // the quotient's sign, also for zero
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = __fdiv_rn(f[i], r.s);
+      if (!FP8) v[i] = fminf(fmaxf(v[i], -127.25f), 127.25f);
+    }
+  }
+  if (!FP8) {
+    // |v| <= 127.25 (+ rounding): adding 1.5 * 2^23 rounds to the nearest
+    // integer (ties to even), left in the low mantissa bits as two's complement
+    uint32_t u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = __float_as_uint(v[i] + 0x1.8p23f);
+    out = v2i{(int)low_bytes(u[0], u[1], u[2], u[3]), (int)low_bytes(u[4], u[5], u[6], u[7])};
+    if (r.zero_row) out = v2i{0, 0};
+    return 0.f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = clamp448(v[i]);
+    out = pack_fp8(v);
+    if (r.zero_row) out = v2i{0, 0};
+    float gs = 0.f;
+    if (GSUM) {
+      gs = __builtin_amdgcn_cvt_f32_fp8(out[0], 0) + __builtin_amdgcn_cvt_f32_fp8(out[0], 1);
+      gs += __builtin_amdgcn_cvt_f32_fp8(out[0], 2);
+      gs += __builtin_amdgcn_cvt_f32_fp8(out[0], 3);
+      gs += __builtin_amdgcn_cvt_f32_fp8(out[1], 0);
+      gs += __builtin_amdgcn_cvt_f32_fp8(out[1], 1);
+      gs += __builtin_amdgcn_cvt_f32_fp8(out[1], 2);
+      gs += __builtin_amdgcn_cvt_f32_fp8(out[1], 3);
+    }
+    return gs;
+  }
+}
+
+// Group sums: a group covers gchunks consecutive chunks, an aligned run of
+// gchunks lanes of one wave (gchunks is a power of two dividing 64); the
+// first lane of the run writes the total.
+__device__ __forceinline__ float group_total(float gs, int gchunks) {
+  for (int off = gchunks >> 1; off > 0; off >>= 1) gs += __shfl_xor(gs, off, kWave);
+  return gs;
+}
+
 template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kQThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int K,
     uint8_t* __restrict__ codes, float* __restrict__ scales,
     float* __restrict__ gsums, int group, const float* __restrict__ static_scale) {
-  __shared__ float red[kQThreads / kWave];
+  __shared__ float red[kQWaves];
   const int m = blockIdx.x;
   const int t = threadIdx.x;
   const uint16_t* xr = x + (int64_t)m * ldx;
   uint8_t* cr = codes + (int64_t)m * K;
   const int nchunks = K >> 3;   // 8 elements per chunk
-
+  // bounds-checked loads, all issued before any is used (zero past the end)
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xr, (uint32_t)K * 2u);
   v4i cache[kQCache];
+#pragma unroll
+  for (int p = 0; p < kQCache; ++p) cache[p] = buffer_load16(xrs, 16u * (uint32_t)(t + p * kQThreads));
   float amax = 0.f;
 #pragma unroll
-  for (int p = 0; p < kQCache; ++p) {
-    const int c = t + p * kQThreads;
-    if (c < nchunks) {
-      cache[p] = *reinterpret_cast<const v4i*>(xr + 8 * c);
-      float f[8];
-      unpack8<BF16>(cache[p], f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    }
-  }
-  for (int c = t + kQCache * kQThreads; c < nchunks; c += kQThreads) {
-    float f[8];
-    unpack8<BF16>(*reinterpret_cast<const v4i*>(xr + 8 * c), f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  }
+  for (int p = 0; p < kQCache; ++p) amax = fmaxf(amax, absmax8<BF16>(cache[p]));
+  for (int c = t + kQCache * kQThreads; c < nchunks; c += kQThreads)
+    amax = fmaxf(amax, absmax8<BF16>(buffer_load16(xrs, 16u * (uint32_t)c)));
   amax = wave_max(amax);
   if ((t & (kWave - 1)) == 0) red[t / kWave] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-  // a static (calibrated, per-tensor) scale replaces the row's own
-  const float s = static_scale ? *static_scale : __fdiv_rn(amax, FP8 ? 448.0f : 127.0f);
-  if (t == 0) scales[m] = s;
-  const bool zero_row = !(s > 0.f);
-  const int gchunks = group >> 3;   // chunks per group (power of two <= 64) for gsums
-
-  auto do_chunk = [&](int c, const v4i raw) {
-    float f[8];
-    unpack8<BF16>(raw, f);
-    uint32_t lo = 0, hi = 0;
-    float gs = 0.f;
-    if (!FP8) {
+  amax = red[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int q = zero_row ? 0 : (int)rintf(__fdiv_rn(f[i], s));
-        q = min(127, max(-127, q));
-        const uint32_t b = (uint32_t)(q & 0xFF);
-        if (i < 4) lo |= b << (8 * i); else hi |= b << (8 * (i - 4));
-      }
+  for (int w = 1; w < kQWaves; ++w) amax = fmaxf(amax, red[w]);
+  amax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(amax)));
+#pragma unroll
+  for (int p = 0; p < kQCache; ++p) asm volatile("" : "+v"(cache[p]));
+
+  const RowScale r = row_scale<FP8>(amax, static_scale);
+  if (t == 0) scales[m] = r.s;
+  const int gchunks = group >> 3;
+  const int ngroups = gsums ? K / group : 0;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(cr, (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(gsums + (int64_t)m * ngroups, (uint32_t)ngroups * 4u);
+
+  // every lane of a wave takes part in the group-sum shuffles; stores past
+  // the row end are dropped
+  auto emit = [&](int c, const v4i raw) {
+    v2i o;
+    if (FP8 && gsums) {
+      const float gs = group_total(quantize_chunk<BF16, FP8, true>(raw, r, o), gchunks);
+      const bool lead = c < nchunks && (c & (gchunks - 1)) == 0;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(gs), grs, lead ? 4u * (uint32_t)(c / gchunks) : kDropped, 0, 0);
     } else {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[i] = zero_row ? 0.f : __fdiv_rn(f[i], s);
-        v[i] = fminf(fmaxf(v[i], -448.f), 448.f);
-      }
-      int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
-      int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
-      lo = (uint32_t)w0;
-      hi = (uint32_t)w1;
-      if (gsums) {
-        gs = __builtin_amdgcn_cvt_f32_fp8(w0, 0) + __builtin_amdgcn_cvt_f32_fp8(w0, 1);
-        gs += __builtin_amdgcn_cvt_f32_fp8(w0, 2);
-        gs += __builtin_amdgcn_cvt_f32_fp8(w0, 3);
-        gs += __builtin_amdgcn_cvt_f32_fp8(w1, 0);
-        gs += __builtin_amdgcn_cvt_f32_fp8(w1, 1);
-        gs += __builtin_amdgcn_cvt_f32_fp8(w1, 2);
-        gs += __builtin_amdgcn_cvt_f32_fp8(w1, 3);
-      }
+      quantize_chunk<BF16, FP8, false>(raw, r, o);
     }
-    *reinterpret_cast<v2i*>(cr + 8 * c) = v2i{(int)lo, (int)hi};
-    return gs;
+    __builtin_amdgcn_raw_buffer_store_b64(o, crs, 8u * (uint32_t)c, 0, 0);
   };
-
-  // Group sums: a group covers gchunks consecutive chunks, i.e. an aligned
-  // run of gchunks lanes inside one wave (gchunks divides 64 and 256).
-  auto emit_gsum = [&](int c, float gs) {
-    if (!FP8 || !gsums) return;
-    for (int off = gchunks >> 1; off > 0; off >>= 1) gs += __shfl_xor(gs, off, kWave);
-    if (c < nchunks && (c % gchunks) == 0) gsums[(int64_t)m * (K / group) + c / gchunks] = gs;
-  };
-
 #pragma unroll
   for (int p = 0; p < kQCache; ++p) {
-    const int c = t + p * kQThreads;
     if (p * kQThreads >= nchunks) break;          // uniform
-    float gs = 0.f;
-    if (c < nchunks) gs = do_chunk(c, cache[p]);
-    emit_gsum(c, gs);
+    emit(t + p * kQThreads, cache[p]);
   }
-  for (int base = kQCache * kQThreads; base < nchunks; base += kQThreads) {
-    const int c = base + t;
-    float gs = 0.f;
-    if (c < nchunks) gs = do_chunk(c, *reinterpret_cast<const v4i*>(xr + 8 * c));
-    emit_gsum(c, gs);
-  }
+  for (int base = kQCache * kQThreads; base < nchunks; base += kQThreads)
+    emit(base + t, buffer_load16(xrs, 16u * (uint32_t)(base + t)));
 }
 
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
                             void* codes, bool fp8, float* scales, float* gsums, int group,
                             hipStream_t stream, const float* static_scale) {
   if (M == 0) return hipSuccess;
-  dim3 grid((unsigned)M), block(kQThreads);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint8_t* cp = static_cast<uint8_t*>(codes);
+  const dim3 grid((unsigned)M), block(kQThreads);
+  const int k = (int)K;
   if (bf16 && !fp8)
-    hipLaunchKernelGGL((quant_act_kernel<true, false>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, nullptr, 8, static_scale);
+    hipLaunchKernelGGL((quant_act_kernel<true, false>), grid, block, 0, stream, xp, ldx, k, cp, scales, nullptr, 8, static_scale);
   else if (!bf16 && !fp8)
-    hipLaunchKernelGGL((quant_act_kernel<false, false>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, nullptr, 8, static_scale);
+    hipLaunchKernelGGL((quant_act_kernel<false, false>), grid, block, 0, stream, xp, ldx, k, cp, scales, nullptr, 8, static_scale);
   else if (bf16 && fp8)
-    hipLaunchKernelGGL((quant_act_kernel<true, true>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, gsums, group, static_scale);
+    hipLaunchKernelGGL((quant_act_kernel<true, true>), grid, block, 0, stream, xp, ldx, k, cp, scales, gsums, group, static_scale);
   else
-    hipLaunchKernelGGL((quant_act_kernel<false, true>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, gsums, group, static_scale);
+    hipLaunchKernelGGL((quant_act_kernel<false, true>), grid, block, 0, stream, xp, ldx, k, cp, scales, gsums, group, static_scale);
   return hipGetLastError();
 }
 
