@@ -6,6 +6,9 @@ quantization followed by the W4A8 GEMM with its fused epilogue, inputs
 resident in HBM. `value` is 2*M*N*K / step time in TOPS.
 
 Measured in the same run and reported beside it:
+  down_proj  W4A8 per-channel down-projection (M=8192, K=14336, N=4096,
+          group -1, fp16 activations with outlier channels): quantization
+          and GEMM times
   decode  W4A16 decode (M=1 and M=8, K=4096, N=14336, group 64), achieved
           HBM GB/s with weights rotated through 16 distinct sets (> MALL)
   moe     W4A-FP8 routed experts (64 experts, K=7168, N=2048, 8192 tokens,
@@ -42,7 +45,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--only", choices=["all", "w4a8", "decode", "moe", "vocab", "shards"], default="all",
+    p.add_argument("--only", choices=["all", "w4a8", "down", "decode", "moe", "vocab", "shards"], default="all",
                    help="which extra measurements to add to the W4A8 step (shards: only when asked for)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     p.add_argument("--crossover", action="store_true",
@@ -185,6 +188,28 @@ def main():
         print(json.dumps({"crossover": {"workload": f"w4_linear K={K} N={N} group={g} bf16", "table": table,
                                         "first_M_int8_faster": cross}}), flush=True)
         return
+
+    # ------------------------------------------------------------ W4A8 per-channel down-proj
+    down = {}
+    if args.only in ("all", "w4a8", "down"):
+        dd = W.named("w4a8_down_proj")
+        Md, Kd, Nd, gd = dd["M"], dd["K"], dd["N"], dd["group"]
+        xd = dev_half(dd["x"], "f16")
+        wtd = ops.w4_repack(torch.from_numpy(dd["qweight"]).to(dev), ops.W4_LAYOUT_GPTQ_KN, Kd, Nd)
+        scd = torch.from_numpy(dd["scales"]).to(dev)
+        codes_d = torch.empty((Md, Kd), dtype=torch.int8, device=dev)
+        s_d = torch.empty((Md,), dtype=torch.float32, device=dev)
+        y_d = torch.empty((Md, Nd), dtype=torch.float16, device=dev)
+        fqd = lambda: ops.quantize_act_into(xd, codes_d, s_d)
+        fgd = lambda: ops.w4a8_gemm(codes_d, s_d, wtd, scd, gd, Nd, out=y_d)
+        (t_qd, t_gd), t_sd, _ = timed([fqd, fgd], max(4, args.steps // 2), max(2, args.warmup // 2))
+        ops_d = 2.0 * Md * Nd * Kd
+        down = {"workload": f"w4a8_down_proj M={Md} K={Kd} N={Nd} group={gd} f16 (1% outlier channels x20)",
+                "quant_ms": t_qd, "gemm_ms": t_gd, "step_ms": t_sd,
+                "gemm_tops": ops_d / (t_gd * 1e-3) / 1e12,
+                "gemm_frac_int8_peak": ops_d / (t_gd * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+                "quant_gbs": (Md * Kd * 3 + Md * 4) / (t_qd * 1e-3) / 1e9}
+        del xd, wtd, codes_d, y_d
 
     # ------------------------------------------------------------ one GPU's share under tensor parallelism (8)
     # column shard: N/8 output columns; row shard: K/8 input columns (its
@@ -331,7 +356,7 @@ def main():
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": w4a8["workload"], "global_batch": M, "seq_len": 1, "parallelism": "single_gpu",
                    "step": "w4a8_quantize_act + w4a8_gemm"},
-        "w4a8": w4a8, "shards": shards, "decode": decode, "prefill": prefill, "moe": moe, "vocab": vocab,
+        "w4a8": w4a8, "down_proj": down, "shards": shards, "decode": decode, "prefill": prefill, "moe": moe, "vocab": vocab,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -67,7 +67,11 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
     int32_t* __restrict__ partials, int M, int N, int K, int KT, int tilesM, int tilesN,
     float* __restrict__ ws, int splits) {
-  constexpr bool kPingPong = ((MODE == kModeGroup || MODE == kModeSplit) && GC == 2);
+  // B straight into registers with three A-only LDS stages: group 128 (its
+  // epilogue interleaved with the MFMAs) and per-channel (whole K summed in
+  // the int32 accumulators, scales applied once after the loop)
+  constexpr bool kPingPong = ((MODE == kModeGroup || MODE == kModeSplit) && GC == 2) || MODE == kModeChannel;
+  constexpr bool kStepScales = kPingPong && MODE != kModeChannel;
   static_assert(MODE != kModeSplit || GC == 2, "split K is built for group 128");
   // group 128: three A-only stages (B stays in registers); otherwise two A+B stages
   constexpr int kSS = kPingPong ? kStageA : kStage;     // bytes per stage
@@ -122,6 +126,8 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // unit (64 wn + 16 j + l%16, l/16); the 64 lanes cover one KiB per block j
   const uint32_t wd_voff = 64u * (uint32_t)(lane & 15) + 16u * (uint32_t)(lane >> 4) + 4096u * (uint32_t)wn;
   v4i pb[kPingPong ? 4 : 2];
+  // per-channel: B two K steps ahead, alternating between pb and pb2
+  v4i pb2[MODE == kModeChannel ? 4 : 1];
   auto gload_a = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
     const uint32_t ks = (uint32_t)tk * kBK;
@@ -131,10 +137,13 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
           arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (32 * wave_u + 8 * i) * kBK), 16,
           a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
   };
-  auto gload_bd = [&](int tk) {
+  auto gload_bd = [&](int tk, auto PBc) {
     const uint32_t ws = (uint32_t)tk * kTileBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pb[j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, wd_voff + 1024u * j, ws, 0);
+    for (int j = 0; j < 4; ++j) {
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, wd_voff + 1024u * j, ws, 0);
+      if constexpr (decltype(PBc)::value == 0) pb[j] = v; else pb2[j] = v;
+    }
   };
   auto gload = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
@@ -290,9 +299,15 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       return;
     }
   }
-  if constexpr (kPingPong) {
-    fetch_scales(kt0, scr_cur);
-    gload_bd(kt0);
+  if constexpr (MODE == kModeChannel) {
+    gload_bd(kt0, IC<0>{});
+    gload_a(kt0, IC<0>{});
+    gload_bd(min(kt0 + 1, kt1 - 1), IC<1>{});
+    gload_a(min(kt0 + 1, kt1 - 1), IC<1>{});
+    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): all but tile 1's B and A
+  } else if constexpr (kPingPong) {
+    if constexpr (kStepScales) fetch_scales(kt0, scr_cur);
+    gload_bd(kt0, IC<0>{});
     gload_a(kt0, IC<0>{});
     gload_a(min(kt0 + 1, kt1 - 1), IC<1>{});
     __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): all but tile 1's A
@@ -308,8 +323,9 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // stored at the end of the step); with three (group 128) A of tile tk + 2,
   // and B of tile tk + 1 into registers. Past the last tile the loads repeat
   // it, which keeps the body branch-free.
-  auto kstep = [&](int tk, auto STc) {
+  auto kstep = [&](int tk, auto STc, auto PBc) {
     constexpr int ST = decltype(STc)::value;
+    constexpr int PB = decltype(PBc)::value;   // per-channel: the B buffer of this step
     // direct path: this step's B words (loaded during the previous step)
     // become fragments before the next step's loads reuse the registers.
     // Substep 0 takes the low nibbles (K 32 q + 0..15 of the lane's quarter
@@ -320,21 +336,42 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          b0[j][e] = (int)(((uint32_t)pb[j][e] << 4) & 0xF0F0F0F0u);
-          b1[j][e] = (int)((uint32_t)pb[j][e] & 0xF0F0F0F0u);
+          const uint32_t w = (uint32_t)(PB == 0 ? pb[j][e] : pb2[j][e]);
+          b0[j][e] = (int)((w << 4) & 0xF0F0F0F0u);
+          b1[j][e] = (int)(w & 0xF0F0F0F0u);
         }
     }
     h2 scr_next[2];
-    if constexpr (kPingPong) {
+    if constexpr (MODE == kModeChannel) {
+      // B of tile tk + 2 into the registers just unpacked, then its A: the
+      // step ends waiting for everything but these eight loads
+      gload_bd(min(tk + 2, kt1 - 1), IC<PB>{});
+      gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
+    } else if constexpr (kPingPong) {
       // loads in this order, A of tile tk + 2 last, so that the step can end
       // waiting for everything but that: vmcnt(4)
-      fetch_scales(min(tk + 1, kt1 - 1), scr_next);
-      gload_bd(min(tk + 1, kt1 - 1));
+      if constexpr (kStepScales) fetch_scales(min(tk + 1, kt1 - 1), scr_next);
+      gload_bd(min(tk + 1, kt1 - 1), IC<0>{});
       gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
     } else {
       gload(min(tk + 1, KT - 1), IC<ST ^ 1>{});
     }
-    if constexpr (kPingPong) {
+    if constexpr (MODE == kModeChannel) {
+      // per-channel: the accumulators run over all of K; low nibbles (b0)
+      // serve chunk 0, high nibbles (b1) chunk 1, for rows 0-1 then 2-3
+      const v4i a00 = read_a(IC<ST>{}, 0, 0), a10 = read_a(IC<ST>{}, 1, 0);
+      const v4i a01 = read_a(IC<ST>{}, 0, 1), a11 = read_a(IC<ST>{}, 1, 1);
+      mfma_row(0, a00, b0, false);
+      mfma_row(1, a10, b0, false);
+      const v4i a20 = read_a(IC<ST>{}, 2, 0), a30 = read_a(IC<ST>{}, 3, 0);
+      mfma_row(0, a01, b1, false);
+      mfma_row(1, a11, b1, false);
+      const v4i a21 = read_a(IC<ST>{}, 2, 1), a31 = read_a(IC<ST>{}, 3, 1);
+      mfma_row(2, a20, b0, false);
+      mfma_row(3, a30, b0, false);
+      mfma_row(2, a21, b1, false);
+      mfma_row(3, a31, b1, false);
+    } else if constexpr (kPingPong) {
       // Four quarters, each eight MFMAs with four vector ALU ops after each:
       //   Q1  rows 0-1, chunk 0 (fresh)  |  rows 2-3 finish group tk - 1 (row 2)
       //   Q2  rows 0-1, chunk 1          |  (row 3)
@@ -396,7 +433,9 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       }
       lstore_b(IC<ST ^ 1>{});
     }
-    if constexpr (kPingPong)
+    if constexpr (MODE == kModeChannel)
+      __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): tile tk + 2's B and A may stay in flight
+    else if constexpr (kPingPong)
       __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): tile tk + 2's A may stay in flight
     else
       wait_loads();
@@ -404,23 +443,38 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   };
 
   int tk = kt0;
-  if constexpr (kPingPong) {
+  if constexpr (MODE == kModeChannel) {
+    // step i = tk - kt0 reads stage i % 3 and B buffer i % 2
+    for (; tk + 5 < kt1; tk += 6) {
+      kstep(tk, IC<0>{}, IC<0>{});
+      kstep(tk + 1, IC<1>{}, IC<1>{});
+      kstep(tk + 2, IC<2>{}, IC<0>{});
+      kstep(tk + 3, IC<0>{}, IC<1>{});
+      kstep(tk + 4, IC<1>{}, IC<0>{});
+      kstep(tk + 5, IC<2>{}, IC<1>{});
+    }
+    if (tk < kt1) kstep(tk, IC<0>{}, IC<0>{});
+    if (tk + 1 < kt1) kstep(tk + 1, IC<1>{}, IC<1>{});
+    if (tk + 2 < kt1) kstep(tk + 2, IC<2>{}, IC<0>{});
+    if (tk + 3 < kt1) kstep(tk + 3, IC<0>{}, IC<1>{});
+    if (tk + 4 < kt1) kstep(tk + 4, IC<1>{}, IC<0>{});
+  } else if constexpr (kPingPong) {
     // stage (tk - kt0) % 3; tile tk + 2 streams in while tk is worked on
     for (; tk + 2 < kt1; tk += 3) {
-      kstep(tk, IC<0>{});
-      kstep(tk + 1, IC<1>{});
-      kstep(tk + 2, IC<2>{});
+      kstep(tk, IC<0>{}, IC<0>{});
+      kstep(tk + 1, IC<1>{}, IC<0>{});
+      kstep(tk + 2, IC<2>{}, IC<0>{});
     }
-    if (tk < kt1) kstep(tk, IC<0>{});
-    if (tk + 1 < kt1) kstep(tk + 1, IC<1>{});
+    if (tk < kt1) kstep(tk, IC<0>{}, IC<0>{});
+    if (tk + 1 < kt1) kstep(tk + 1, IC<1>{}, IC<0>{});
   } else {
     for (; tk + 1 < KT; tk += 2) {
-      kstep(tk, IC<0>{});
-      kstep(tk + 1, IC<1>{});
+      kstep(tk, IC<0>{}, IC<0>{});
+      kstep(tk + 1, IC<1>{}, IC<0>{});
     }
-    if (tk < KT) kstep(tk, IC<0>{});
+    if (tk < KT) kstep(tk, IC<0>{}, IC<0>{});
   }
-  if constexpr (kPingPong) epilogue(IC<2>{}, IC<4>{}, scr_prev, kt1 - 1);
+  if constexpr (kStepScales) epilogue(IC<2>{}, IC<4>{}, scr_prev, kt1 - 1);
   if constexpr (MODE == kModePartials) return;
   if constexpr (MODE == kModeSplit) {
     // fp32 partial tile with the row scale applied: rows of 16 columns are

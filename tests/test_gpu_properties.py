@@ -132,7 +132,8 @@ def test_canaries_w4a8_and_weight_only(M, K, N, group):
         assert canaries_intact(tbuf)
 
 
-@pytest.mark.parametrize("M,K,N,group", [(1, 4096, 1000, 64), (13, 192, 24, 64), (16, 1536, 72, 512)])
+@pytest.mark.parametrize("M,K,N,group", [(1, 4096, 1000, 64), (13, 192, 24, 64), (16, 1536, 72, 512),
+                                         (8, 512, 14336, 64), (1, 256, 9000, 128)])
 def test_canaries_decode(M, K, N, group):
     d = W.w4a16_inputs(M, K, N, group, seed=M + K)
     wt, stl = ops.w4a16_repack(torch.from_numpy(d["w"]).to(DEV), dev_half(d["scale"], "bf16"),
