@@ -160,7 +160,9 @@ int w4_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch,
  *   out       device, [M, N] in out_dtype (W4_BF16 or W4_F16), 16-byte
  *             aligned (rows are written in 16-byte segments)
  * Errors: INVALID, ALIGN (K or N % 8; w_tiled, out not 16-byte aligned; a
- *         not 8-byte aligned), GROUP, DTYPE, HIP. M == 0 or N == 0 enqueues
+ *         not 8-byte aligned), GROUP, DTYPE, UNSUPPORTED (a K-group, or K
+ *         with group -1, above 132096: the int32 sums of 16 * a * (q - 8)
+ *         over a group could overflow), HIP. M == 0 or N == 0 enqueues
  *         nothing.
  */
 int w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled,
@@ -274,7 +276,8 @@ int w4a16_tiled_gemm(const void* x, int x_dtype, const void* w_tiled, const void
  *             caller owns it; calls sharing one workspace must not overlap.
  *   x, out    device, 16-byte aligned; out [M, N] in the activation dtype
  *   other arguments as w4a16_tiled_gemm.
- * Errors: those of the path taken, and INVALID when the workspace is too small.
+ * Errors: those of the path taken (UNSUPPORTED for a K-group above 132096,
+ *         as w4a8_gemm, whatever M), and INVALID when the workspace is too small.
  */
 #define W4_LINEAR_MIN_TOKENS_INT8 33
 int w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group, int64_t min_tokens_int8,

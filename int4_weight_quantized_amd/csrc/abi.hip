@@ -166,6 +166,19 @@ int w4_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch, 
   return hip_status(w4::launch_repack(src, layout, K, N, batch, dst, static_cast<hipStream_t>(stream)), fn);
 }
 
+// The int8 kernels sum 16 * a * (q - 8) over a whole group in int32 (the
+// nibble is unpacked as a byte 16 (q - 8)): |sum| <= 16 * 127 * 8 * group,
+// below 2^31 for groups of at most 132096 (= K for per-channel weights).
+constexpr int64_t kMaxInt8Group = 132096;
+static int check_int32_range(const char* fn, int64_t group, int64_t K) {
+  const int64_t g = group == -1 ? K : group;
+  if (g > kMaxInt8Group)
+    return fail(W4_ERR_UNSUPPORTED,
+                "%s: a K-group of %lld exceeds %lld, the largest whose int32 partial sums cannot overflow", fn,
+                (long long)g, (long long)kMaxInt8Group);
+  return W4_OK;
+}
+
 static int check_gemm(const char* fn, const int8_t* a, const void* w_tiled, int64_t group, int64_t M, int64_t N,
                       int64_t K) {
   int rc = check_mnk(fn, M, N, K);
@@ -173,6 +186,8 @@ static int check_gemm(const char* fn, const int8_t* a, const void* w_tiled, int6
   if (group != -1 && (group <= 0 || group % 64 || K % group))
     return fail(W4_ERR_GROUP, "%s: group size %lld must be -1 (per channel) or a multiple of 64 dividing K=%lld", fn,
                 (long long)group, (long long)K);
+  rc = check_int32_range(fn, group, K);
+  if (rc) return rc;
   if (M == 0 || N == 0) return W4_OK;
   if (!a || !w_tiled) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
   if (!aligned16(w_tiled)) return fail(W4_ERR_ALIGN, "%s: w_tiled must be 16-byte aligned", fn);
@@ -356,6 +371,8 @@ int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_sca
               size_t workspace_bytes, void* stream) {
   const char* fn = "w4_linear";
   int rc = check_tiled(fn, x, x_dtype, w_tiled, w_scale, scale_dtype, group, M, N, K);
+  if (rc) return rc;
+  rc = check_int32_range(fn, group, K);
   if (rc) return rc;
   if (M == 0 || N == 0) return ok();
   if (!out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);

@@ -68,6 +68,22 @@ def test_group_rules(L):
                                8, 8, 256, 256, None) == -3
 
 
+def test_int32_group_limit(L):
+    """The int8 kernels sum 16*a*(q-8) over a K-group in int32: per-channel K
+    (or a group) above 132096 is refused before anything is launched, with
+    the sizes named; 132096 itself passes validation (and then stops at the
+    null pointers)."""
+    K_bad, K_ok = 132096 + 8, 132096
+    rc = L.w4a8_gemm(None, None, None, None, 2, -1, None, None, 1, 16, 256, K_bad, None)
+    assert rc == -5 and b"132104" in L.w4_last_error()
+    assert L.w4a8_gemm(None, None, None, None, 2, -1, None, None, 1, 16, 256, K_ok, None) == -1
+    assert L.w4a8_gemm_partials(None, None, -1, None, 16, 256, K_bad, None) == -5
+    assert L.w4a8_gemm(None, None, None, None, 2, 132096 + 64, None, None, 1, 16, 256, 2 * (132096 + 64), None) == -5
+    buf = ctypes.create_string_buffer(64)
+    ptr = ctypes.c_void_p((ctypes.addressof(buf) + 15) & ~15)      # never dereferenced: validation fails first
+    assert L.w4_linear(ptr, 1, ptr, ptr, 2, -1, None, ptr, 16, 256, K_bad, 1, None, 0, None) == -5
+
+
 def test_output_alignment(L):
     # the GEMM writes 16-byte row segments: a misaligned output is refused
     p = ctypes.c_void_p
