@@ -149,6 +149,7 @@ def _w4a8_dev(d):
 EDGE_SHAPES = [  # (M, K, N, group)
     (1, 64, 8, -1), (5, 8, 8, -1), (130, 200, 24, -1), (33, 192, 136, 64),
     (17, 512, 256, 256), (129, 384, 264, 128), (64, 1024, 512, 128), (3, 14336, 16, -1),
+    (9, 384, 40, -1), (67, 640, 136, -1), (200, 1408, 264, -1),
 ]
 
 
