@@ -474,6 +474,9 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     }
     if (tk < KT) kstep(tk, IC<0>{}, IC<0>{});
   }
+  // the last steps' A tiles may still be streaming into LDS: no wave leaves
+  // (or reuses LDS) with its own DMA in flight
+  __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
   if constexpr (kStepScales) epilogue(IC<2>{}, IC<4>{}, scr_prev, kt1 - 1);
   if constexpr (MODE == kModePartials) return;
   if constexpr (MODE == kModeSplit) {
@@ -520,6 +523,9 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   constexpr int kORow = kBN * 2 + 16;                    // padded output row in LDS, bytes
   static_assert(kBM * kORow <= kNS * kSS, "output tile fits the stage buffers");
   const int orow0 = 64 * wm + 4 * (lane >> 4), ocol0 = 64 * wn + (lane & 15);
+  // every wave has drained its A tiles (above) before any overwrites the
+  // stage buffers with the output
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
