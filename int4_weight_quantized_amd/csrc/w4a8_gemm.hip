@@ -9,13 +9,15 @@
 //   out[m,n] = a_scale[m] * sum_g w_scale[g,n] * P[m,g,n] + bias[n]
 //
 // Design (gfx950):
-// - 256 threads, block tile 128x128, four waves of 64x64, K step 128, two
-//   LDS stages (64 KiB) so two blocks share a CU and their waves interleave
-//   on each SIMD.
-// - Loads are raw buffer loads issued one K step ahead of use. A (int8
-//   codes) goes straight from memory to LDS, its range check zero-filling
-//   rows past M; B (the tiled int4 layout, 8 KiB contiguous per tile) comes
-//   through registers.
+// - 256 threads, block tile 128x128, four waves of 64x64, K step 128.
+//   Group 128 and per-channel: three A-only LDS stages (48 KiB), A two K
+//   steps ahead, B straight into registers (one step ahead for group 128,
+//   two for per-channel, in alternating register sets); two blocks per CU
+//   (three for per-channel at 166 VGPRs). Other group sizes and the partials
+//   hook: two A+B stages (64 KiB), loads one step ahead.
+// - Loads are raw buffer loads. A (int8 codes) goes straight from memory to
+//   LDS, its range check zero-filling rows past M; B is the tiled int4
+//   layout, 8 KiB contiguous per tile.
 // - B (stored nibble q^8) becomes int8 bytes 16*(q-8) with a mask (and a
 //   4-bit shift); the MFMA accumulates 16*P and 1/16 is folded into the row
 //   scale (exact). With group 128 each wave loads its own 64 columns straight
@@ -24,7 +26,10 @@
 //   low nibbles serve the first 64-deep MFMA step and the high nibbles the
 //   second, and the A fragments carry the same K assignment (chunk 2q +
 //   step, stored where the bank-conflict-free read pattern finds it). That
-//   halves the LDS traffic. The other modes unpack B once per block into LDS.
+//   halves the LDS traffic. Per-channel weights use the same loads; the
+//   int32 accumulators then run over all of K and the column scale is
+//   applied once after the loop. The two-stage modes unpack B once per
+//   block into LDS.
 // - A and B rows in LDS are 128 bytes; 16-byte chunk kc of row r sits at
 //   kc ^ (r & 7). Fragment reads and tile writes are then bank-conflict free
 //   (measured), and every fragment address is a base register plus an
@@ -425,11 +430,11 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       for (int c = 0; c < 2; ++c) {
         const int cg = cg0 + c;
         if (cg >= nchunks) break;
-        const bool fresh = (MODE == kModeChannel) ? (cg == 0) : (cg % group_chunks == 0);
+        const bool fresh = cg % group_chunks == 0;
         v4i bf[4];
         read_b(IC<ST>{}, c, bf);
         mfma_rows(IC<ST>{}, c, IC<0>{}, IC<4>{}, fresh, bf);
-        if (MODE != kModeChannel && (cg + 1) % group_chunks == 0) epilogue(IC<0>{}, IC<4>{}, c ? s1 : s0, cg / group_chunks);
+        if ((cg + 1) % group_chunks == 0) epilogue(IC<0>{}, IC<4>{}, c ? s1 : s0, cg / group_chunks);
       }
       lstore_b(IC<ST ^ 1>{});
     }
