@@ -101,6 +101,42 @@ def quantize_act_int8_static(x32: np.ndarray, s) -> np.ndarray:
     return np.clip(np.rint(x32 / s), -127, 127).astype(np.int8)
 
 
+def quantize_act_int8_asym(x32: np.ndarray):
+    """Per-token asymmetric int8: x32 float32 [M, K] -> (codes int8 [M, K],
+    scale float32 [M], offset float32 [M]) with x ~ code * scale + offset.
+
+    [ct_w4a8] __init__ carries an input_symmetric flag and [inc_w4a8]
+    apply_weights passes the per-token quant op's zero output to the GEMM;
+    neither page prints the asymmetric arithmetic. READING: the min/max grid
+    of [cpu_int4] quantize_groupwise (scale = (max - min) / (levels - 1),
+    codes counted from min, an additive offset in value units) with 256
+    levels, in fp32:
+        d = fl32(max - min),  scale = fl32(d / 255),
+        code = clamp(rne(fl32(fl32(x - min) / scale)), 0, 255) - 128,
+        offset = fl32(min + 128 * scale).
+    A constant row has scale 0, codes -128 and offset = min (exact). Inputs
+    whose fp32 range max - min overflows are outside the reading."""
+    x32 = np.asarray(x32, dtype=F32)
+    assert np.all(np.isfinite(x32)), "oracle assumes finite activations"
+    M, K = x32.shape
+    codes = np.full((M, K), -128, dtype=np.int8)
+    if K == 0:
+        z = np.zeros(M, F32)
+        return codes, z, z.copy()
+    lo = np.min(x32, axis=1).astype(F32)
+    hi = np.max(x32, axis=1).astype(F32)
+    d = (hi - lo).astype(F32)
+    assert np.all(np.isfinite(d)), "row range overflows fp32"
+    scale = (d / F32(255.0)).astype(F32)
+    offset = (lo + F32(128.0) * scale).astype(F32)        # 128 * scale is exact
+    nz = scale > 0
+    if np.any(nz):
+        t = (x32[nz] - lo[nz][:, None]).astype(F32)        # fp32, rounded once
+        q = (t / scale[nz][:, None]).astype(F32)           # fp32 / fp32, correctly rounded
+        codes[nz] = (np.clip(np.rint(q), 0, 255) - 128).astype(np.int8)
+    return codes, scale, offset
+
+
 def e4m3_decode(codes) -> np.ndarray:
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     sign = np.where(c >> 7, -1.0, 1.0)
@@ -301,6 +337,33 @@ def w4a8_reference(x_bits, x_dtype, qweight, scales_f16, group, bias_bits=None, 
     bias = None if bias_bits is None else half_bits_to_f32(bias_bits, x_dtype)
     y = w4a8_epilogue(P, a_scale[r], np.asarray(scales_f16, dtype=np.float32), bias)
     return dict(codes=codes, a_scale=a_scale, P=P, y=y, rows=r)
+
+
+def weight_offsets(q_kn: np.ndarray, scales_gn, group: int) -> np.ndarray:
+    """C[n] = sum_g scale[g, n] * sum_{k in g} (q[k, n] - 8), float64: what an
+    activation offset z contributes to output column n per unit of z, since
+    sum_k z * (q[k, n] - 8) * scale[k // g, n] = z * C[n]."""
+    K = q_kn.shape[0]
+    g_eff = effective_group(group, K)
+    S = np.asarray(scales_gn, dtype=np.float64)
+    W = (q_kn.astype(np.int64) - 8).reshape(K // g_eff, g_eff, -1).sum(axis=1)   # exact integers
+    return (S * W).sum(axis=0)
+
+
+def w4a8_reference_asym(x_bits, x_dtype, qweight, scales_f16, group, bias_bits=None, rows=None):
+    """W4A8 forward with asymmetric per-token activations on the original
+    layouts: y = sum_k (code * s + z) * (q - 8) * scale (+ bias)
+              = s * sum_g scale * P + z * C[n] (+ bias), float64."""
+    x32 = half_bits_to_f32(x_bits, x_dtype)
+    codes, a_scale, a_off = quantize_act_int8_asym(x32)
+    q = unpack_gptq_kn(qweight)
+    r = np.arange(codes.shape[0]) if rows is None else np.asarray(rows)
+    P = group_partials(codes[r], q, group)
+    S = np.asarray(scales_f16, dtype=np.float32)
+    bias = None if bias_bits is None else half_bits_to_f32(bias_bits, x_dtype)
+    y = w4a8_epilogue(P, a_scale[r], S, bias)
+    y += np.asarray(a_off[r], dtype=np.float64)[:, None] * weight_offsets(q, S, group)[None, :]
+    return dict(codes=codes, a_scale=a_scale, a_offset=a_off, P=P, y=y, rows=r)
 
 
 # --------------------------------------------------------------------------

@@ -511,3 +511,72 @@ def test_static_int8_quantizer():
     codes, s = O.quantize_act_int8(xr)
     for m in range(5):
         assert np.array_equal(O.quantize_act_int8_static(xr[m:m + 1], s[m]), codes[m:m + 1])
+
+
+# ------------------------------------------------------------------ asymmetric activations
+
+def test_asym_int8_worked_example():
+    """Hand-worked (reading of [ct_w4a8] input_symmetric=False on the [cpu_int4]
+    min/max grid): row [0, 100.5, 101.5, 255, 37] has min 0, max 255, so the
+    step is exactly 1 and the offset 0 + 128 = 128. Code + 128 counts steps
+    from the minimum: 0, 100.5 -> 100 and 101.5 -> 102 (ties to even), 255, 37.
+    Scaling the row by 2**-3 scales step and offset and keeps the codes."""
+    x = np.array([[0, 100.5, 101.5, 255, 37]], dtype=np.float32)
+    want = np.array([[-128, -28, -26, 127, -91]], dtype=np.int8)
+    for k in (0, -3, 5):
+        c, s, z = O.quantize_act_int8_asym(x * np.float32(2.0 ** k))
+        assert np.array_equal(c, want) and s[0] == 2.0 ** k and z[0] == 128 * 2.0 ** k
+    # shifted by -40: min -40 -> offset -40 + 128, same codes
+    c, s, z = O.quantize_act_int8_asym(x - np.float32(40))
+    assert np.array_equal(c, want) and s[0] == 1 and z[0] == 88
+
+
+def test_asym_int8_invariants_and_constant_rows():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((64, 300)) * rng.uniform(0.01, 30, (64, 1)) + rng.uniform(-5, 5, (64, 1)))
+    x = x.astype(np.float32)
+    c, s, z = O.quantize_act_int8_asym(x)
+    lo, hi = x.min(1), x.max(1)
+    for m in range(64):
+        # the grid spans the row: its minimum sits on code -128, its maximum on 127
+        assert c[m, np.argmin(x[m])] == -128 and c[m, np.argmax(x[m])] == 127
+        # every value is within half a step (plus fp32 slack) of its grid point
+        deq = c[m].astype(np.float64) * s[m] + z[m]
+        assert np.all(np.abs(deq - x[m]) <= 0.5 * s[m] * (1 + 1e-5) + 1e-6 * (abs(lo[m]) + abs(hi[m])))
+        # codes are monotone in x
+        o = np.argsort(x[m], kind="stable")
+        assert np.all(np.diff(c[m][o].astype(np.int32)) >= 0)
+        # the step is the range over 255 levels
+        assert abs(float(s[m]) - (float(hi[m]) - float(lo[m])) / 255) <= 1e-6 * float(s[m])
+    # a constant row: no step, every code at -128, offset = the value (exact)
+    cc, sc, zc = O.quantize_act_int8_asym(np.full((2, 7), -3.25, dtype=np.float32))
+    assert np.all(cc == -128) and np.all(sc == 0) and np.all(zc == np.float32(-3.25))
+
+
+def test_asym_epilogue_vs_dequantize_then_matmul():
+    """y = sum_k (code*s + z) * (q-8) * scale, the definition, against the
+    factored s * sum_g scale * P + z * C[n] the reference computes; plus the
+    constant-row special case y[n] = value * C[n] and C against a loop."""
+    rng = np.random.default_rng(5)
+    M, K, N = 5, 256, 24
+    for group in (64, -1):
+        G = 1 if group == -1 else K // group
+        x = rng.standard_normal((M, K)).astype(np.float32) + np.float32(1.5)
+        x[3] = np.float32(0.75)                                   # constant row
+        xb = (x.view(np.uint32) >> 16).astype(np.uint16)          # bf16 bits (truncated: any bf16 input)
+        qw = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32).view(np.int32)
+        sc = rng.uniform(0.005, 0.02, (G, N)).astype(np.float16)
+        ref = O.w4a8_reference_asym(xb, "bf16", qw, sc, group)
+        x32 = O.bf16_bits_to_f32(xb)
+        c, s, z = O.quantize_act_int8_asym(x32)
+        q = O.unpack_gptq_kn(qw).astype(np.float64)
+        g_eff = K if group == -1 else group
+        Wd = (q - 8) * np.repeat(sc.astype(np.float64), g_eff, axis=0)
+        Xd = c.astype(np.float64) * s.astype(np.float64)[:, None] + z.astype(np.float64)[:, None]
+        assert np.allclose(ref["y"], Xd @ Wd, rtol=1e-12, atol=1e-12)
+        C = np.zeros(N)
+        for n in range(N):
+            for k in range(K):
+                C[n] += (q[k, n] - 8) * float(sc[k // g_eff, n])
+        assert np.allclose(O.weight_offsets(O.unpack_gptq_kn(qw), sc, group), C, rtol=1e-12, atol=1e-12)
+        assert np.allclose(ref["y"][3], float(x32[3, 0]) * C, rtol=1e-12, atol=1e-12)
