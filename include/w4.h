@@ -117,6 +117,52 @@ int w4a8_quantize_act_static(const void* x, int x_dtype, int64_t M, int64_t K, i
                              float* group_sums, int64_t group, void* stream);
 
 /*
+ * Per-token asymmetric int8 activation quantization. [ct_w4a8]
+ * CompressedTensorsW4A8Int takes an input_symmetric flag and [inc_w4a8]
+ * apply_weights hands the per-token quant op's zero output to the int8 GEMM;
+ * neither page prints the asymmetric arithmetic. Reading: the min/max grid
+ * of [cpu_int4] quantize_groupwise with 256 levels, per row, in fp32:
+ *   scale  = (max - min) / 255
+ *   code   = clamp(rne((x - min) / scale), 0, 255) - 128   (fp32 divide)
+ *   offset = min + 128 * scale          so that x ~ code * scale + offset
+ * A constant row gives scale 0, codes -128 and offset = min.
+ *   x        device, [M, K] bf16/fp16 with row stride ldx (16-byte aligned)
+ *   codes    device, int8 [M, K] (8-byte aligned)
+ *   scales, offsets  device, fp32 [M]
+ * Rows whose fp32 range (max - min) overflows are outside the reading.
+ * Errors: INVALID, ALIGN (K % 8, ldx, alignment), DTYPE, UNSUPPORTED, HIP.
+ */
+int w4a8_quantize_act_asym(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                           int8_t* codes, float* scales, float* offsets, void* stream);
+
+/*
+ * Load-time per-column weight offsets for asymmetric activations:
+ *   out[n] = sum_g w_scale[g, n] * sum_{k in g} (q[k, n] - 8)   (fp32)
+ * An activation offset z adds z * out[n] to output n, since
+ * sum_k z * (q[k, n] - 8) * w_scale[k / group, n] = z * out[n].
+ *   w_tiled, w_scale, group, K, N  as w4a8_gemm;  out: device, fp32 [N]
+ * Errors: INVALID, ALIGN, GROUP, DTYPE, HIP.
+ */
+int w4a8_weight_offsets(const void* w_tiled, const void* w_scale, int scale_dtype, int64_t group,
+                        int64_t K, int64_t N, float* out, void* stream);
+
+/*
+ * W4A8 GEMM with asymmetric per-token activations (codes, scales and
+ * offsets from w4a8_quantize_act_asym):
+ *   out[m,n] = a_scale[m] * sum_g w_scale[g,n] * P[m,g,n]
+ *            + a_offset[m] * w_offsets[n] + bias[n]
+ * with P the int32 group sums of w4a8_gemm (the same kernel; the offset
+ * term joins the bias in its fp32 epilogue).
+ *   a_offset   device, fp32 [M];  w_offsets: device, fp32 [N] from
+ *              w4a8_weight_offsets for the same weights, scales and group
+ *   other arguments, layouts and errors as w4a8_gemm.
+ */
+int w4a8_gemm_asym(const int8_t* a, const float* a_scale, const float* a_offset, const void* w_tiled,
+                   const void* w_scale, int scale_dtype, int64_t group, const float* w_offsets,
+                   const void* bias, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                   void* stream);
+
+/*
  * Size in bytes of one weight matrix in the kernel-tiled layout produced by
  * w4_repack (tiles of 128 output columns x 128 K, 8 KiB each, ragged edges
  * padded with code 8, i.e. zero weight).

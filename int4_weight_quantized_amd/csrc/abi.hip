@@ -17,7 +17,12 @@ hipError_t launch_repack(const void* src, int layout, int64_t K, int64_t N, int6
                          hipStream_t stream);
 hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled, const void* w_scale,
                             int64_t group, const void* bias, void* out, bool out_bf16, int32_t* partials,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                            const float* a_off = nullptr, const float* w_off = nullptr);
+hipError_t launch_quant_act_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, void* codes,
+                                 float* scales, float* offsets, hipStream_t stream);
+hipError_t launch_weight_offsets(const void* w_tiled, const void* w_scale, int64_t group, int64_t K, int64_t N,
+                                 float* out, hipStream_t stream);
 void w4a16_tiled_bytes(int64_t K, int64_t N, size_t* wbytes, size_t* szbytes);
 int w4a8_split_count(int64_t M, int64_t N, int64_t K, int64_t group);
 hipError_t launch_w4a8_gemm_split(const int8_t* a, const float* a_scale, const void* w_tiled, const void* w_scale,
@@ -223,6 +228,63 @@ int w4a8_gemm_partials(const int8_t* a, const void* w_tiled, int64_t group, int3
   if (!partials) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
   return hip_status(w4::launch_w4a8_gemm(a, nullptr, w_tiled, nullptr, group, nullptr, nullptr, true, partials, M, N,
                                          K, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int w4a8_quantize_act_asym(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t* codes,
+                           float* scales, float* offsets, void* stream) {
+  const char* fn = "w4a8_quantize_act_asym";
+  if (M < 0 || K < 0) return fail(W4_ERR_INVALID, "%s: negative size M=%lld K=%lld", fn, (long long)M, (long long)K);
+  if (x_dtype != W4_BF16 && x_dtype != W4_F16)
+    return fail(W4_ERR_DTYPE, "%s: activations must be bf16 or fp16 (dtype code %d)", fn, x_dtype);
+  if (K % 8) return fail(W4_ERR_ALIGN, "%s: K=%lld is not a multiple of 8", fn, (long long)K);
+  if (M > kMaxDim || K > ((int64_t)1 << 24))
+    return fail(W4_ERR_UNSUPPORTED, "%s: sizes too large (M=%lld K=%lld)", fn, (long long)M, (long long)K);
+  if (ldx < K || ldx % 8)
+    return fail(W4_ERR_ALIGN, "%s: ldx=%lld must be >= K=%lld and a multiple of 8", fn, (long long)ldx,
+                (long long)K);
+  if (M == 0) return ok();
+  if (!x || !codes || !scales || !offsets) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(x)) return fail(W4_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(codes) & 7u) != 0) return fail(W4_ERR_ALIGN, "%s: codes must be 8-byte aligned", fn);
+  return hip_status(w4::launch_quant_act_asym(x, x_dtype == W4_BF16, M, K, ldx, codes, scales, offsets,
+                                              static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int w4a8_weight_offsets(const void* w_tiled, const void* w_scale, int scale_dtype, int64_t group, int64_t K,
+                        int64_t N, float* out, void* stream) {
+  const char* fn = "w4a8_weight_offsets";
+  if (scale_dtype != W4_F16) return fail(W4_ERR_DTYPE, "%s: weight scales must be fp16 (dtype code %d)", fn, scale_dtype);
+  int rc = check_mnk(fn, 0, N, K);
+  if (rc) return rc;
+  if (group != -1 && (group <= 0 || group % 64 || K % group))
+    return fail(W4_ERR_GROUP, "%s: group size %lld must be -1 (per channel) or a multiple of 64 dividing K=%lld", fn,
+                (long long)group, (long long)K);
+  if (N == 0) return ok();
+  if (!w_tiled || !w_scale || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(w_tiled)) return fail(W4_ERR_ALIGN, "%s: w_tiled must be 16-byte aligned", fn);
+  return hip_status(w4::launch_weight_offsets(w_tiled, w_scale, group, K, N, out, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int w4a8_gemm_asym(const int8_t* a, const float* a_scale, const float* a_offset, const void* w_tiled,
+                   const void* w_scale, int scale_dtype, int64_t group, const float* w_offsets, const void* bias,
+                   void* out, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  const char* fn = "w4a8_gemm_asym";
+  if (scale_dtype != W4_F16)
+    return fail(W4_ERR_DTYPE, "%s: weight scales must be fp16 (dtype code %d); the int8 kernel reads them as fp16",
+                fn, scale_dtype);
+  if (out_dtype != W4_BF16 && out_dtype != W4_F16)
+    return fail(W4_ERR_DTYPE, "%s: output must be bf16 or fp16 (dtype code %d)", fn, out_dtype);
+  int rc = check_gemm(fn, a, w_tiled, group, M, N, K);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return ok();
+  if (!a_scale || !a_offset || !w_scale || !w_offsets || !out)
+    return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(out)) return fail(W4_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+  return hip_status(w4::launch_w4a8_gemm(a, a_scale, w_tiled, w_scale, group, bias, out, out_dtype == W4_BF16,
+                                         nullptr, M, N, K, static_cast<hipStream_t>(stream), a_offset, w_offsets),
                     fn);
 }
 

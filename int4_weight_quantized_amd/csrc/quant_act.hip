@@ -222,6 +222,91 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(
     emit(base + t, buffer_load16(xrs, 16u * (uint32_t)(base + t)));
 }
 
+// Per-token asymmetric int8 (the input_symmetric = False variant of the
+// compressed-tensors W4A8 scheme; the zero output of the inc W4A8 layer's
+// per-token quant op). The pages print no arithmetic for it; the grid is the
+// min/max one of the cpu_int4 page's quantize_groupwise with 256 levels, in
+// fp32:
+//   scale  = (max - min) / 255
+//   code   = clamp(rne((x - min) / scale), 0, 255) - 128
+//   offset = min + 128 * scale            so that x ~ code * scale + offset
+// A constant row has scale 0, codes -128 and offset = min.
+// One block per row: a min/max pass (wave shuffles, then LDS), then the
+// codes, 8 per 16-byte load and 8-byte store; the division is IEEE
+// correctly rounded, the decision the codes are taken on.
+template <bool BF16>
+__global__ __launch_bounds__(kQThreads) void quant_act_asym_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                   int K, uint8_t* __restrict__ codes,
+                                                                   float* __restrict__ scales,
+                                                                   float* __restrict__ offsets) {
+  __shared__ float s_lo[kQWaves], s_hi[kQWaves];
+  const int64_t m = blockIdx.x;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + m * ldx, (uint32_t)K * 2u);
+  const int nchunks = K >> 3;
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  for (int c = t; c < nchunks; c += kQThreads) {
+    float f[8];
+    unpack8<BF16>(buffer_load16(xrs, 16u * (uint32_t)c), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo = fminf(lo, f[i]);
+      hi = fmaxf(hi, f[i]);
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off, kWave));
+    hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+  }
+  if (lane == 0) {
+    s_lo[wv] = lo;
+    s_hi[wv] = hi;
+  }
+  __syncthreads();
+  lo = s_lo[0];
+  hi = s_hi[0];
+#pragma unroll
+  for (int w = 1; w < kQWaves; ++w) {
+    lo = fminf(lo, s_lo[w]);
+    hi = fmaxf(hi, s_hi[w]);
+  }
+  const float scale = __fdiv_rn(hi - lo, 255.f);
+  const float offset = lo + 128.f * scale;              // 128 * scale is exact
+  if (t == 0) {
+    scales[m] = scale;
+    offsets[m] = offset;
+  }
+  uint8_t* cr = codes + m * (int64_t)K;
+  for (int c = t; c < nchunks; c += kQThreads) {
+    float f[8];
+    unpack8<BF16>(buffer_load16(xrs, 16u * (uint32_t)c), f);
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q = scale > 0.f ? rintf(__fdiv_rn(f[i] - lo, scale)) : 0.f;
+      b[i] = (uint32_t)((int)fminf(fmaxf(q, 0.f), 255.f) - 128) & 0xFFu;
+    }
+    uint2 pk;
+    pk.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    pk.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    *reinterpret_cast<uint2*>(cr + 8 * (int64_t)c) = pk;
+  }
+}
+
+hipError_t launch_quant_act_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, void* codes,
+                                 float* scales, float* offsets, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint8_t* cp = static_cast<uint8_t*>(codes);
+  const dim3 grid((unsigned)M), block(kQThreads);
+  if (bf16)
+    hipLaunchKernelGGL((quant_act_asym_kernel<true>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, offsets);
+  else
+    hipLaunchKernelGGL((quant_act_asym_kernel<false>), grid, block, 0, stream, xp, ldx, (int)K, cp, scales, offsets);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
                             void* codes, bool fp8, float* scales, float* gsums, int group,
                             hipStream_t stream, const float* static_scale) {

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
     int32_t* __restrict__ partials, int M, int N, int K, int KT, int tilesM, int tilesN,
-    float* __restrict__ ws, int splits) {
+    float* __restrict__ ws, int splits, const float* __restrict__ a_off, const float* __restrict__ w_off) {
   // B straight into registers with three A-only LDS stages: group 128 (its
   // epilogue interleaved with the MFMAs) and per-channel (whole K summed in
   // the int32 accumulators, scales applied once after the loop)
@@ -512,7 +512,18 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // (free after the loop's last barrier) so that each thread then writes
   // whole 16-byte row segments: 8 vector stores per thread instead of 64
   // 2-byte ones. N is a multiple of 8, so a segment is all in or all out.
+  // asymmetric activations add a_off[m] * w_off[n] (activation offset times
+  // the column's weight offset sum) to the bias term
   float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  float wo[4] = {0.f, 0.f, 0.f, 0.f}, ao[4][4] = {};
+  if (a_off) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wo[j] = w_off[min(ncol[j], N - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ao[i][r] = a_off[min(mrow0 + 16 * i + r, M - 1)];
+  }
   if (bias) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -537,7 +548,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float y = fmaf(facc[i][j][r], sa[i][r], bv[j]);
+        const float y = fmaf(facc[i][j][r], sa[i][r], fmaf(ao[i][r], wo[j], bv[j]));
         *reinterpret_cast<uint16_t*>(lds + (orow0 + 16 * i + r) * kORow + 2 * (ocol0 + 16 * j)) =
             OUT_BF16 ? f32_to_bf16_rne(y) : f32_to_f16_rne(y);
       }
@@ -554,7 +565,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
 hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled,
                             const void* w_scale, int64_t group, const void* bias, void* out,
                             bool out_bf16, int32_t* partials, int64_t M, int64_t N, int64_t K,
-                            hipStream_t stream) {
+                            hipStream_t stream, const float* a_off, const float* w_off) {
   if (M == 0 || N == 0) return hipSuccess;
   const int KT = (int)((K + kBK - 1) / kBK);
   const int tilesM = (int)((M + kBM - 1) / kBM), tilesN = (int)((N + kBN - 1) / kBN);
@@ -568,7 +579,7 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
   const int iM = (int)M, iN = (int)N, iK = (int)K;
 #define W4A8_LAUNCH(MODE_, BF16_, GC_)                                                                  \
   hipLaunchKernelGGL((w4a8_gemm_kernel<MODE_, BF16_, GC_>), grid, block, 0, stream, a, a_scale, W, S, gc, B, O, \
-                     partials, iM, iN, iK, KT, tilesM, tilesN, nullptr, 1)
+                     partials, iM, iN, iK, KT, tilesM, tilesN, nullptr, 1, a_off, w_off)
   if (partials) {
     W4A8_LAUNCH(kModePartials, true, 0);
   } else if (group == -1) {
@@ -640,6 +651,48 @@ __global__ __launch_bounds__(256) void split_finalize_kernel(const float* __rest
   *reinterpret_cast<v4i*>(out + e0) = pk;
 }
 
+// Per-column weight offsets for asymmetric activations:
+//   C[n] = sum_g w_scale[g, n] * sum_{k in g} (q[k, n] - 8)
+// so that an activation offset z adds z * C[n] to output n. Load-time, from
+// the tiled weights: one thread per column walks its 16-byte units (32
+// codes each, stored q ^ 8 = the two's-complement nibble of q - 8), sums
+// each group exactly in integers and accumulates scale * sum in fp32.
+__global__ __launch_bounds__(256) void weight_offsets_kernel(const uint8_t* __restrict__ Wt,
+                                                             const uint16_t* __restrict__ wscale, int N, int K,
+                                                             int KT, int gsz, float* __restrict__ out) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const uint8_t* col = Wt + (int64_t)(n / kTileN) * KT * kTileBytes + 64 * (n % kTileN);
+  float c = 0.f;
+  int gsum = 0;
+  for (int k0 = 0; k0 < K; k0 += 32) {                  // unit: 32 codes of K 32kq .. 32kq+31
+    const v4i u = *reinterpret_cast<const v4i*>(col + (int64_t)(k0 / kTileK) * kTileBytes + 16 * ((k0 % kTileK) / 32));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int v = ((uint32_t)u[e] >> (4 * i)) & 0xF;
+        gsum += v - ((v & 8) << 1);                      // signed nibble = q - 8
+      }
+    if ((k0 + 32) % gsz == 0 || k0 + 32 >= K) {         // a group ends (per channel: K may end mid-unit, padded with zeros)
+      c = fmaf(f16_to_f32(wscale[(int64_t)(k0 / gsz) * N + n]), (float)gsum, c);
+      gsum = 0;
+    }
+  }
+  out[n] = c;
+}
+
+hipError_t launch_weight_offsets(const void* w_tiled, const void* w_scale, int64_t group, int64_t K, int64_t N,
+                                 float* out, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int KT = (int)((K + kBK - 1) / kBK);
+  const int gsz = group == -1 ? (int)K : (int)group;
+  hipLaunchKernelGGL(weight_offsets_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(w_tiled), static_cast<const uint16_t*>(w_scale), (int)N, (int)K,
+                     KT, gsz, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_w4a8_gemm_split(const int8_t* a, const float* a_scale, const void* w_tiled, const void* w_scale,
                                   const void* bias, void* out, bool out_bf16, int64_t M, int64_t N, int64_t K,
                                   int splits, float* ws, hipStream_t stream) {
@@ -650,7 +703,7 @@ hipError_t launch_w4a8_gemm_split(const int8_t* a, const float* a_scale, const v
   hipLaunchKernelGGL((w4a8_gemm_kernel<kModeSplit, true, 2>), grid, block, 0, stream, a, a_scale,
                      static_cast<const v4i*>(w_tiled), static_cast<const uint16_t*>(w_scale), 2,
                      static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(nullptr), nullptr, (int)M, (int)N,
-                     (int)K, KT, tilesM, tilesN, ws, splits);
+                     (int)K, KT, tilesM, tilesN, ws, splits, nullptr, nullptr);
   const int64_t MN = M * N;
   dim3 fgrid((unsigned)((MN / 8 + 255) / 256));
   auto B = static_cast<const uint16_t*>(bias);

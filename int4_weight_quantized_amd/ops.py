@@ -39,6 +39,9 @@ _SIGS = {
     "w4a16_dequantize": [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
     "w4_quantize_groupwise": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P],
     "w4a16_embedding": [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P],
+    "w4a8_quantize_act_asym": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P],
+    "w4a8_weight_offsets": [_P, _P, _I, _I64, _I64, _I64, _P, _P],
+    "w4a8_gemm_asym": [_P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _I, _I64, _I64, _I64, _P],
     "w4_last_error": [],
     "w4_version": [],
 }
@@ -134,6 +137,39 @@ def w4a8_quantize_act_static(x: torch.Tensor, static_scale: torch.Tensor, code_d
         _ptr(x), _half_code(x.dtype), M, K, K, _ptr(static_scale), _ptr(codes), W4_FP8_E4M3 if fp8 else W4_I8,
         _ptr(scales), _ptr(gs), group_sums_group or 0, _stream(stream)))
     return codes, scales, gs
+
+
+def w4a8_quantize_act_asym(x: torch.Tensor, stream=None):
+    """x [M, K] bf16/fp16 -> (codes int8 [M, K], scales fp32 [M], offsets fp32 [M]),
+    x ~ code * scale + offset per row."""
+    M, K = x.shape
+    codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    offsets = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check("w4a8_quantize_act_asym", lib().w4a8_quantize_act_asym(
+        _ptr(x), _half_code(x.dtype), M, K, K, _ptr(codes), _ptr(scales), _ptr(offsets), _stream(stream)))
+    return codes, scales, offsets
+
+
+def w4a8_weight_offsets(w_tiled, w_scale, group: int, K: int, N: int, stream=None) -> torch.Tensor:
+    """fp32 [N]: sum_g w_scale[g, n] * sum_{k in g} (q[k, n] - 8), from the tiled weights."""
+    out = torch.empty((N,), dtype=torch.float32, device=w_tiled.device)
+    sdt = W4_F16 if w_scale.dtype == torch.float16 else (W4_BF16 if w_scale.dtype == torch.bfloat16 else W4_F32)
+    _check("w4a8_weight_offsets", lib().w4a8_weight_offsets(
+        _ptr(w_tiled), _ptr(w_scale), sdt, group, K, N, _ptr(out), _stream(stream)))
+    return out
+
+
+def w4a8_gemm_asym(a, a_scale, a_offset, w_tiled, w_scale, group: int, w_offsets, N: int,
+                   out_dtype=torch.bfloat16, bias=None, out=None, stream=None):
+    M, K = a.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    sdt = W4_F16 if w_scale.dtype == torch.float16 else (W4_BF16 if w_scale.dtype == torch.bfloat16 else W4_F32)
+    _check("w4a8_gemm_asym", lib().w4a8_gemm_asym(
+        _ptr(a), _ptr(a_scale), _ptr(a_offset), _ptr(w_tiled), _ptr(w_scale), sdt, group, _ptr(w_offsets),
+        _ptr(bias), _ptr(out), _half_code(out.dtype), M, N, K, _stream(stream)))
+    return out
 
 
 def w4_repack_bytes(K: int, N: int) -> int:

@@ -478,3 +478,69 @@ def test_w4a16_prefill_path(M, N, K, group):
                                          O.bf16_bits_to_f32(d["zero"]), group))
     bound = 2.0 ** -7 * (np.abs(x) @ wabs.T) + 2.0 ** -7 * np.abs(ref) + 1e-3
     assert np.all(np.abs(to_f64(y) - ref) <= bound)
+
+
+# ------------------------------------------------------------------ asymmetric activations
+
+@pytest.mark.parametrize("name", ["w4a8_tiny", "w4a8_up_proj", "w4a8_down_proj"])
+def test_quant_asym_workloads_bit_exact(name):
+    d = W.named(name)
+    print(f"\n[quant asym] {name} M={d['M']} K={d['K']}", flush=True)
+    x = dev_half(d["x"], d["x_dtype"])
+    codes, s, z = ops.w4a8_quantize_act_asym(x)
+    rc, rs, rz = O.quantize_act_int8_asym(O.half_bits_to_f32(d["x"], d["x_dtype"]))
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(z.cpu().numpy(), rz)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("K", [8, 72, 4096, 20000])
+def test_quant_asym_edges(dtype, K):
+    rng = np.random.default_rng(K + (dtype == "f16"))
+    M = 37
+    x = (rng.standard_normal((M, K)) * rng.uniform(0.01, 50, (M, 1)) + rng.uniform(-20, 20, (M, 1)))
+    x[3] = 1.5                                    # constant row
+    x[4] = 0.0                                    # all zeros
+    x[5, :] = np.abs(x[5, :])                     # one-signed row
+    bits = W.to_half_bits(x.astype(np.float32), dtype)
+    codes, s, z = ops.w4a8_quantize_act_asym(dev_half(bits, dtype))
+    rc, rs, rz = O.quantize_act_int8_asym(O.half_bits_to_f32(bits, dtype))
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(z.cpu().numpy(), rz)
+
+
+ASYM_SHAPES = [(16, 256, 256, 128), (1, 64, 8, -1), (130, 200, 24, -1), (33, 192, 136, 64),
+               (129, 384, 264, 128), (64, 1024, 512, 256), (9, 640, 40, -1)]
+
+
+@pytest.mark.parametrize("M,K,N,group", ASYM_SHAPES)
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_w4a8_asym_gemm(M, K, N, group, out_dtype):
+    d = W.w4a8_inputs(M, K, N, group, out_dtype, seed=M + 5 * K + N, with_bias=True)
+    x, wt, sc = _w4a8_dev(d)
+    # shift the activations so the rows are far from symmetric
+    xs = (x.float() + 2.0).to(x.dtype)
+    xs_bits = xs.view(torch.int16).cpu().numpy().view(np.uint16)
+    codes, s, z = ops.w4a8_quantize_act_asym(xs)
+    woff = ops.w4a8_weight_offsets(wt, sc, group, K, N)
+    bias = dev_half(d["bias"], out_dtype)
+    y = ops.w4a8_gemm_asym(codes, s, z, wt, sc, group, woff, N, out_dtype=xs.dtype, bias=bias)
+    ref = O.w4a8_reference_asym(xs_bits, out_dtype, d["qweight"], d["scales"], group, bias_bits=d["bias"])
+    assert np.array_equal(codes.cpu().numpy(), ref["codes"])
+    Cref = O.weight_offsets(O.unpack_gptq_kn(d["qweight"]), d["scales"].astype(np.float32), group)
+    assert np.allclose(woff.cpu().numpy().astype(np.float64), Cref, rtol=1e-5, atol=1e-5)
+    assert_close(to_f64(y), ref["y"], f"w4a8 asym {M}x{K}x{N} g{group} {out_dtype}")
+
+
+def test_w4a8_asym_up_proj_rows():
+    """The up-projection workload with asymmetric activations, at full size;
+    the oracle on a row sample."""
+    d = W.named("w4a8_up_proj")
+    x, wt, sc = _w4a8_dev(d)
+    codes, s, z = ops.w4a8_quantize_act_asym(x)
+    woff = ops.w4a8_weight_offsets(wt, sc, d["group"], d["K"], d["N"])
+    y = ops.w4a8_gemm_asym(codes, s, z, wt, sc, d["group"], woff, d["N"], out_dtype=x.dtype)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(8).choice(d["M"], 32, replace=False))
+    ref = O.w4a8_reference_asym(d["x"], d["x_dtype"], d["qweight"], d["scales"], d["group"], rows=rows)
+    assert_close(to_f64(y[torch.from_numpy(rows).to(DEV)]), ref["y"], "w4a8 asym up_proj")

@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     for must in ("w4a8_quantize_act", "w4a8_gemm", "w4a16_gemm", "w4a16_repack", "w4a8_grouped_gemm", "w4_repack",
                  "w4_repack_bytes", "w4a8_gemm_partials", "w4a16_tiled_gemm", "w4_linear", "w4_linear_workspace_bytes",
                  "w4_quantize_groupwise", "w4a16_embedding", "w4a8_quantize_act_static", "w4a16_dequantize",
+                 "w4a8_quantize_act_asym", "w4a8_weight_offsets", "w4a8_gemm_asym",
                  "w4_last_error", "w4_version"):
         assert must in names
 
@@ -147,3 +148,18 @@ def test_linear_workspace_and_dispatch_checks(L):
     assert L.w4a16_tiled_gemm(p(256), 1, p(256), p(256), 2, 128, None, p(256), 17, 256, 4096, None) == -5
     assert L.w4a16_tiled_gemm(p(256), 1, p(256), p(256), 1, 128, None, p(256), 4, 256, 4096, None) == -4
     assert L.w4a16_tiled_gemm(p(256), 1, p(256), p(256), 2, 96, None, p(256), 4, 256, 4096, None) == -3
+
+
+def test_asym_entry_points_validate(L):
+    """Asymmetric activations: argument checks on the host, before any launch."""
+    assert L.w4a8_quantize_act_asym(None, 1, 4, 12, 12, None, None, None, None) == -2        # K % 8
+    assert L.w4a8_quantize_act_asym(None, 7, 4, 16, 16, None, None, None, None) == -4        # dtype
+    assert L.w4a8_quantize_act_asym(None, 1, 4, 16, 16, None, None, None, None) == -1        # null
+    assert L.w4a8_quantize_act_asym(None, 1, 0, 16, 16, None, None, None, None) == 0         # empty
+    assert L.w4a8_weight_offsets(None, None, 1, 128, 256, 256, None, None) == -4             # bf16 scales
+    assert L.w4a8_weight_offsets(None, None, 2, 96, 288, 256, None, None) == -3              # group
+    assert L.w4a8_weight_offsets(None, None, 2, 128, 256, 256, None, None) == -1             # null
+    assert L.w4a8_gemm_asym(None, None, None, None, None, 2, 128, None, None, None, 1, 16, 256, 256, None) == -1
+    assert L.w4a8_gemm_asym(None, None, None, None, None, 1, 128, None, None, None, 1, 16, 256, 256, None) == -4
+    assert L.w4a8_gemm_asym(None, None, None, None, None, 2, 96, None, None, None, 1, 16, 256, 288, None) == -3
+    assert L.w4a8_gemm_asym(None, None, None, None, None, 2, 128, None, None, None, 1, 0, 256, 256, None) == 0
