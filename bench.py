@@ -6,6 +6,8 @@ quantization followed by the W4A8 GEMM with its fused epilogue, inputs
 resident in HBM. `value` is 2*M*N*K / step time in TOPS.
 
 Measured in the same run and reported beside it:
+  asym    the same layer with asymmetric per-token activations
+          (w4a8_quantize_act_asym + w4a8_gemm_asym)
   down_proj  W4A8 per-channel down-projection (M=8192, K=14336, N=4096,
           group -1, fp16 activations with outlier channels): quantization
           and GEMM times
@@ -189,6 +191,18 @@ def main():
                                         "first_M_int8_faster": cross}}), flush=True)
         return
 
+    # ------------------------------------------------------------ asymmetric activations, same layer
+    asym = {}
+    if args.only in ("all", "w4a8"):
+        z_a = torch.empty((M,), dtype=torch.float32, device=dev)
+        woff = ops.w4a8_weight_offsets(wt, sc, g, K, N)
+        fqa = lambda: ops.w4a8_quantize_act_asym_into(x, codes, s_a, z_a)
+        fga = lambda: ops.w4a8_gemm_asym(codes, s_a, z_a, wt, sc, g, woff, N, out=y)
+        (t_qa, t_ga), t_sa, _ = timed([fqa, fga], max(4, args.steps // 2), max(2, args.warmup // 2))
+        asym = {"workload": f"w4a8_up_proj asymmetric per-token activations M={M} K={K} N={N} group={g}",
+                "quant_ms": t_qa, "gemm_ms": t_ga, "step_ms": t_sa,
+                "gemm_tops": ops_gemm / (t_ga * 1e-3) / 1e12}
+
     # ------------------------------------------------------------ W4A8 per-channel down-proj
     down = {}
     if args.only in ("all", "w4a8", "down"):
@@ -356,7 +370,7 @@ def main():
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": w4a8["workload"], "global_batch": M, "seq_len": 1, "parallelism": "single_gpu",
                    "step": "w4a8_quantize_act + w4a8_gemm"},
-        "w4a8": w4a8, "down_proj": down, "shards": shards, "decode": decode, "prefill": prefill, "moe": moe, "vocab": vocab,
+        "w4a8": w4a8, "asym": asym, "down_proj": down, "shards": shards, "decode": decode, "prefill": prefill, "moe": moe, "vocab": vocab,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

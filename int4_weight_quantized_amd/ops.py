@@ -146,9 +146,14 @@ def w4a8_quantize_act_asym(x: torch.Tensor, stream=None):
     codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
     scales = torch.empty((M,), dtype=torch.float32, device=x.device)
     offsets = torch.empty((M,), dtype=torch.float32, device=x.device)
+    w4a8_quantize_act_asym_into(x, codes, scales, offsets, stream)
+    return codes, scales, offsets
+
+
+def w4a8_quantize_act_asym_into(x, codes, scales, offsets, stream=None):
+    M, K = x.shape
     _check("w4a8_quantize_act_asym", lib().w4a8_quantize_act_asym(
         _ptr(x), _half_code(x.dtype), M, K, K, _ptr(codes), _ptr(scales), _ptr(offsets), _stream(stream)))
-    return codes, scales, offsets
 
 
 def w4a8_weight_offsets(w_tiled, w_scale, group: int, K: int, N: int, stream=None) -> torch.Tensor:
