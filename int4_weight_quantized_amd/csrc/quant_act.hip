@@ -233,7 +233,9 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(
 // A constant row has scale 0, codes -128 and offset = min.
 // One block per row: a min/max pass (wave shuffles, then LDS), then the
 // codes, 8 per 16-byte load and 8-byte store; the division is IEEE
-// correctly rounded, the decision the codes are taken on.
+// correctly rounded, the decision the codes are taken on. Each thread keeps
+// its first kQCache 16-byte chunks in registers between the two passes
+// (rows up to 16384 elements are read once); longer rows re-read the rest.
 template <bool BF16>
 __global__ __launch_bounds__(kQThreads) void quant_act_asym_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                    int K, uint8_t* __restrict__ codes,
@@ -245,15 +247,23 @@ __global__ __launch_bounds__(kQThreads) void quant_act_asym_kernel(const uint16_
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + m * ldx, (uint32_t)K * 2u);
   const int nchunks = K >> 3;
   float lo = __builtin_inff(), hi = -__builtin_inff();
-  for (int c = t; c < nchunks; c += kQThreads) {
+  auto minmax = [&](const v4i raw) {
     float f[8];
-    unpack8<BF16>(buffer_load16(xrs, 16u * (uint32_t)c), f);
+    unpack8<BF16>(raw, f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       lo = fminf(lo, f[i]);
       hi = fmaxf(hi, f[i]);
     }
-  }
+  };
+  v4i cache[kQCache];
+#pragma unroll
+  for (int i = 0; i < kQCache; ++i)   // past the row end: out-of-range loads read zero, never used
+    cache[i] = buffer_load16(xrs, 16u * (uint32_t)(t + kQThreads * i));
+#pragma unroll
+  for (int i = 0; i < kQCache; ++i)
+    if (t + kQThreads * i < nchunks) minmax(cache[i]);
+  for (int c = t + kQCache * kQThreads; c < nchunks; c += kQThreads) minmax(buffer_load16(xrs, 16u * (uint32_t)c));
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
     lo = fminf(lo, __shfl_xor(lo, off, kWave));
@@ -278,9 +288,9 @@ __global__ __launch_bounds__(kQThreads) void quant_act_asym_kernel(const uint16_
     offsets[m] = offset;
   }
   uint8_t* cr = codes + m * (int64_t)K;
-  for (int c = t; c < nchunks; c += kQThreads) {
+  auto emit = [&](int c, const v4i raw) {
     float f[8];
-    unpack8<BF16>(buffer_load16(xrs, 16u * (uint32_t)c), f);
+    unpack8<BF16>(raw, f);
     uint32_t b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -291,7 +301,11 @@ __global__ __launch_bounds__(kQThreads) void quant_act_asym_kernel(const uint16_
     pk.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
     pk.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
     *reinterpret_cast<uint2*>(cr + 8 * (int64_t)c) = pk;
-  }
+  };
+#pragma unroll
+  for (int i = 0; i < kQCache; ++i)
+    if (t + kQThreads * i < nchunks) emit(t + kQThreads * i, cache[i]);
+  for (int c = t + kQCache * kQThreads; c < nchunks; c += kQThreads) emit(c, buffer_load16(xrs, 16u * (uint32_t)c));
 }
 
 hipError_t launch_quant_act_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, void* codes,
