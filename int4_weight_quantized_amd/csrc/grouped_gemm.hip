@@ -19,8 +19,9 @@
 // - Block tile 128 rows x 128 columns, 4 waves of 64x64, K step 128, two LDS
 //   stages. Activation rows are gathered by token id straight into LDS (LDS
 //   DMA: each lane's source row is its token's); rows past the segment read
-//   as zero. B comes through registers, 8 KiB contiguous per tile, and is
-//   unpacked once per block. 16-byte LDS chunks are swizzled by row & 7 and
+//   as zero. B comes through registers two K steps ahead (two register
+//   sets), 8 KiB contiguous per tile, and is unpacked once per block into
+//   LDS one step ahead; a step then waits only for its next A tile. 16-byte LDS chunks are swizzled by row & 7 and
 //   lane group g reads chunks g and g + 4: bank-conflict free.
 // - A two-half schedule like the W4A8 kernel's (epilogue of one half under
 //   the other half's MFMAs) does not fit the registers here: the fp8
@@ -102,9 +103,11 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   const __amdgpu_buffer_rsrc_t gsrc = make_rsrc(gsum, (uint32_t)((int64_t)T * G * 4));
   const int my_tok = (tid < kEM) ? s_tok[tid] : -1;
   const uint32_t g_voff = (my_tok >= 0) ? (uint32_t)my_tok * (uint32_t)G * 4u : 0x80000000u;
-  v4i pb[2];
-  float pgs = 0.f;
-  auto gload = [&](int tk, auto STc) {
+  // B words and group sums of step t sit in pb[t & 1] / pgs[t & 1]: they are
+  // loaded two steps ahead and stored into LDS one step ahead
+  v4i pb[2][2];
+  float pgs[2] = {0.f, 0.f};
+  auto gload_a = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
     const uint32_t ks = (uint32_t)tk * kEK;
 #pragma unroll
@@ -112,11 +115,16 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kEStage + (32 * wave_u + 8 * i) * kEK), 16,
           a_voff[i] + ks, 0, 0, 0);
+  };
+  // three loads per call for every wave (the group sum of a row without a
+  // token, or of a thread past the tile's rows, reads as zero from past the
+  // buffer), so a step can wait for its A tile with a fixed vmcnt(3)
+  auto gload_bg = [&](int tk, auto Pc) {
+    constexpr int P = decltype(Pc)::value;
     const uint32_t ws = (uint32_t)tk * kTileBytes;
-    pb[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws, 0);
-    pb[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws + 4096u, 0);
-    if (wave_u < 2 && (tk % GT) == 0)
-      pgs = -8.f * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, g_voff + 4u * (uint32_t)(tk / GT), 0, 0));
+    pb[P][0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws, 0);
+    pb[P][1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws + 4096u, 0);
+    pgs[P] = -8.f * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, g_voff + 4u * (uint32_t)(tk / GT), 0, 0));
   };
   // B unit u (row n = u/4, K quarter q = u%4): low nibbles -> logical chunk
   // 2q (K 32q+0..15), high nibbles -> chunk 2q+1, as fp8 codes q.
@@ -125,13 +133,13 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   auto lstore = [&](auto STc, int tk) {
     constexpr int ST = decltype(STc)::value;
     uint8_t* lb = lds + ST * kEStage + kEStageA;
-    if (wave_u < 2 && (tk % GT) == 0) s_gs[ST][tid] = pgs;
+    if (wave_u < 2 && (tk % GT) == 0) s_gs[ST][tid] = pgs[ST];   // stage ST holds a step of parity ST
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       v4i lo, hi;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t x = (uint32_t)pb[i][c] ^ 0x88888888u;   // stored q^8 -> q
+        const uint32_t x = (uint32_t)pb[ST][i][c] ^ 0x88888888u;   // stored q^8 -> q
         lo[c] = (int)(x & 0x0F0F0F0Fu);
         hi[c] = (int)((x >> 4) & 0x0F0F0F0Fu);
       }
@@ -208,20 +216,26 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   };
 
   // ---- prologue
-  gload(0, EC<0>{});
+  gload_a(0, EC<0>{});
+  gload_bg(0, EC<0>{});
   lstore(EC<0>{}, 0);
+  gload_bg(min(1, KT - 1), EC<1>{});
   wait_loads();
   __syncthreads();
 
   // K step tk reads stage ST = tk & 1 while tile tk + 1 streams into the
-  // other stage (A by DMA, B through registers stored at the end of the
-  // step). Past the last tile the loads repeat it: the body is branch-free.
+  // other stage: A by DMA, B (loaded into registers during step tk - 1)
+  // unpacked and stored at the end of the step. Past the last tile the
+  // loads repeat it: the body is branch-free.
   auto kstep = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
-    gload(min(tk + 1, KT - 1), EC<ST ^ 1>{});
+    // this step's scales, then A of tk + 1, then B of tk + 2: the step ends
+    // waiting for all but the last three loads (B and the group sums)
     const bool fresh = (tk % GT) == 0, last = (tk % GT) == GT - 1;
     uint32_t sc[4];
     fetch_scales(tk / GT, sc);
+    gload_a(min(tk + 1, KT - 1), EC<ST ^ 1>{});
+    gload_bg(min(tk + 2, KT - 1), EC<ST>{});        // into the registers stored last step
     v8i bf[4];
     read_b(EC<ST>{}, bf);
     // one row's A fragment and C init at a time (bounds the live registers)
@@ -232,7 +246,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     }
     if (last) epilogue(EC<0>{}, EC<4>{}, sc);
     lstore(EC<ST ^ 1>{}, tk + 1);
-    wait_loads();
+    __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3): A of step tk + 1 landed; step tk + 2's B may stay in flight
     __syncthreads();
   };
 
