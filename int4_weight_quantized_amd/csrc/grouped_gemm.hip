@@ -21,8 +21,9 @@
 //   DMA: each lane's source row is its token's); rows past the segment read
 //   as zero. B comes through registers two K steps ahead (two register
 //   sets), 8 KiB contiguous per tile, and is unpacked once per block into
-//   LDS one step ahead; a step then waits only for its next A tile. 16-byte LDS chunks are swizzled by row & 7 and
-//   lane group g reads chunks g and g + 4: bank-conflict free.
+//   LDS one step ahead; a step then waits only for its next A tile.
+//   16-byte LDS chunks are swizzled by row & 7 and lane group g reads
+//   chunks g and g + 4: bank-conflict free.
 // - A two-half schedule like the W4A8 kernel's (epilogue of one half under
 //   the other half's MFMAs) does not fit the registers here: the fp8
 //   fragments are twice as wide, and it spills. The epilogue follows each
