@@ -57,6 +57,29 @@ def test_w4a8_layer_random_shapes(shape):
     assert np.array_equal(P.cpu().numpy().astype(np.int64), ref["P"])
 
 
+@SETTINGS
+@given(w4a8_shapes())
+def test_w4a8_asym_random_shapes(shape):
+    """Asymmetric activations (shifted so rows are one-signed or skewed):
+    codes, scales and offsets bit-exact, outputs within tolerance."""
+    M, K, N, group, dtype, bias, seed = shape
+    d = W.w4a8_inputs(M, K, N, group, dtype, seed=seed, with_bias=bias)
+    shift = np.float32((seed % 7) - 3)
+    x32 = O.half_bits_to_f32(d["x"], dtype) + shift
+    xb = W.to_half_bits(x32, dtype)
+    x = dev_half(xb, dtype)
+    wt = ops.w4_repack(torch.from_numpy(d["qweight"]).to(DEV), ops.W4_LAYOUT_GPTQ_KN, K, N)
+    sc = torch.from_numpy(d["scales"]).to(DEV)
+    b = dev_half(d["bias"], dtype) if bias else None
+    codes, s, z = ops.w4a8_quantize_act_asym(x)
+    woff = ops.w4a8_weight_offsets(wt, sc, group, K, N)
+    y = ops.w4a8_gemm_asym(codes, s, z, wt, sc, group, woff, N, out_dtype=x.dtype, bias=b)
+    ref = O.w4a8_reference_asym(xb, dtype, d["qweight"], d["scales"], group, bias_bits=d["bias"])
+    assert np.array_equal(codes.cpu().numpy(), ref["codes"])
+    assert np.array_equal(s.cpu().numpy(), ref["a_scale"]) and np.array_equal(z.cpu().numpy(), ref["a_offset"])
+    assert close(y, ref["y"]), (M, K, N, group, dtype, bias, seed)
+
+
 @st.composite
 def decode_shapes(draw):
     group = draw(st.sampled_from([64, 128, 256, 512]))
@@ -125,6 +148,21 @@ def test_canaries_w4a8_and_weight_only(M, K, N, group):
     ops.w4_linear(x, wt, sc, group, N, bias=b, out=yl.view(M, N))          # dispatch (split K when few rows)
     torch.cuda.synchronize()
     assert canaries_intact(cbuf) and canaries_intact(sbuf) and canaries_intact(ybuf) and canaries_intact(lbuf)
+    # asymmetric path: codes, scales, offsets, weight offsets and output
+    abuf, ac = padded(M * K, torch.int8)
+    asbuf, a_s = padded(M, torch.float32)
+    azbuf, a_z = padded(M, torch.float32)
+    ops.w4a8_quantize_act_asym_into(x, ac.view(M, K), a_s, a_z)
+    wobuf, wo = padded(N, torch.float32)
+    wo.copy_(ops.w4a8_weight_offsets(wt, sc, group, K, N))
+    wo2buf, wo2 = padded(N, torch.float32)
+    _check_offsets = ops.lib().w4a8_weight_offsets(ops._ptr(wt), ops._ptr(sc), ops.W4_F16, group, K, N,
+                                                  ops._ptr(wo2), ops._stream(None))
+    assert _check_offsets == 0
+    yabuf, ya = padded(M * N, torch.bfloat16)
+    ops.w4a8_gemm_asym(ac.view(M, K), a_s, a_z, wt, sc, group, wo, N, bias=b, out=ya.view(M, N))
+    torch.cuda.synchronize()
+    assert all(canaries_intact(t) for t in (abuf, asbuf, azbuf, wo2buf, yabuf))
     if M <= 16:
         tbuf, yt = padded(M * N, torch.bfloat16)
         ops.w4a16_tiled_gemm(x, wt, sc, group, N, bias=b, out=yt.view(M, N))
