@@ -285,6 +285,48 @@ def dequantize_groupwise(q, scale, zero, group: int) -> np.ndarray:
     return (q - 8.0) * s + z
 
 
+def f32_to_bf16_bits(v32) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to the even bf16):
+    keep the upper 16 bits, add one unit in their last place when the lower
+    16 bits exceed half of it, or equal half of it and the kept part is odd.
+    Finite inputs only."""
+    u = np.asarray(v32, dtype=F32).view(np.uint32).astype(np.uint64)
+    kept = u >> np.uint64(16)
+    low = u & np.uint64(0xFFFF)
+    up = (low > 0x8000) | ((low == 0x8000) & ((kept & np.uint64(1)) == 1))
+    return (kept + up.astype(np.uint64)).astype(np.uint16)
+
+
+def dequantize_bf16(q, scale_bits, zero_bits, group: int) -> np.ndarray:
+    """[cpu_int4] dequantize / _dequantize_halves, the prefill path: the weight
+    w = (q - 8) * scale + zero unpacked to a bf16 matrix [N, K] (returned as
+    bf16 bit patterns) for the ordinary bf16 GEMM.
+
+    READING: the page hands the bf16 expression to torch.compile, which
+    evaluates it in float32 and rounds once, to bf16, when it stores the
+    result. So: (q - 8) * scale in float32 (exact: a 4-bit integer times an
+    8-bit significand), + zero rounded to float32, then rounded to bf16,
+    nearest even. (Evaluated op by op in bf16, each of the two operations
+    would round to bf16.)"""
+    q = np.asarray(q, dtype=np.uint8)
+    n, k = q.shape
+    s = np.repeat(bf16_bits_to_f32(scale_bits), group, axis=1)
+    z = np.repeat(bf16_bits_to_f32(zero_bits), group, axis=1)
+    prod = (q.astype(F32) - F32(8.0)) * s
+    w32 = (prod + z).astype(F32)
+    assert w32.dtype == F32
+    return f32_to_bf16_bits(w32)
+
+
+def w4a16_prefill_reference(x_bits, w_bytes, scale_bits, zero_bits, group: int) -> np.ndarray:
+    """[cpu_int4] _cpu_int4_linear, batches at or above the threshold: the
+    bf16 activations times the transposed bf16 weight of dequantize_bf16,
+    y [M, N] in float64 (the GEMM itself exact)."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    Wb = bf16_bits_to_f32(dequantize_bf16(unpack_nibble_bytes(w_bytes), scale_bits, zero_bits, group))
+    return x @ Wb.astype(np.float64).T
+
+
 # --------------------------------------------------------------------------
 # W4A8 GEMM. [inc_w4a8] apply_weights: int8 codes with per-token scales,
 # int4 weights with per-group fp16 scales, bias fused; output in the

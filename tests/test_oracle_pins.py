@@ -147,6 +147,88 @@ def test_fp8_act_quant_rows():
     assert np.all(np.abs(dec[nz][big] - xs[big]) <= np.abs(xs[big]) * 2.0 ** -4 + 1e-12)
 
 
+def _e4m3_nearest_by_midpoints(q32: np.ndarray) -> np.ndarray:
+    """E4M3 code of float32 values by the format's definition, written out
+    with midpoints: the positive finite codes 0x00..0x7E increase with their
+    exact values; |q| (saturated at 448) takes the code whose interval between
+    neighbouring midpoints holds it, and on a midpoint itself the even code of
+    the two. Midpoints of E4M3 values are exact in binary64, so the
+    comparisons are exact. The sign bit is the input's."""
+    vals = [_e4m3_value_exact(c) for c in range(127)]
+    assert all(a < b for a, b in zip(vals[:-1], vals[1:]))
+    mids = np.array([float((vals[i] + vals[i + 1]) / 2) for i in range(126)])
+    assert all(Fraction(m) == (vals[i] + vals[i + 1]) / 2 for i, m in enumerate(mids))
+    a = np.minimum(np.abs(np.asarray(q32, dtype=np.float64)), 448.0)
+    below = np.searchsorted(mids, a, side="left")          # midpoints strictly below |q|
+    on_mid = (below < 126) & (mids[np.minimum(below, 125)] == a)
+    code = np.where(on_mid & (below % 2 == 1), below + 1, below)
+    return (code.astype(np.uint8) | (np.signbit(q32).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def test_fp8_bruteforce_all_bf16_patterns():
+    """Every finite bf16 value, placed in rows of fixed absmax (powers of two
+    and not), against exact arithmetic: scale = f32(amax/448) (a binary64
+    divide rounded to binary32 is the correctly rounded binary32 quotient),
+    code = E4M3 of f32(x/scale) by midpoints. A reciprocal multiply, a
+    float64 scale or quotient, or a wrong tie rule fails here."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = O.bf16_bits_to_f32(bits)
+    v = v[np.isfinite(v)]
+    for amax in (1.0, 3.0, 7.25, 0.3, 1e-3, 448.0):
+        amax32 = np.float32(amax)
+        row = v[np.abs(v) <= amax32]
+        x = np.concatenate([[amax32], row]).astype(np.float32)[None, :]
+        codes, s = O.quantize_act_fp8(x)
+        s_ref = _f32(float(amax32) / 448.0)
+        assert float(s[0]) == s_ref, amax
+        q32 = np.array([_f32(float(t) / s_ref) for t in x[0]], dtype=np.float32)
+        ref = _e4m3_nearest_by_midpoints(q32)
+        assert np.array_equal(codes[0], ref), (amax, int(np.sum(codes[0] != ref)))
+        assert O.e4m3_decode(codes[:, :1])[0, 0] == 448.0       # the absmax itself maps to 448
+
+
+def test_fp8_quantizer_midpoint_rows():
+    """Rows whose quotients sit exactly on E4M3 midpoints and one float32 step
+    either side: scale 1 (absmax 448), so x/scale = x."""
+    vals = [_e4m3_value_exact(c) for c in range(127)]
+    mids = [np.float32(float((a + b) / 2)) for a, b in zip(vals[:-1], vals[1:])]
+    row = [np.float32(448.0)]
+    for m in mids:
+        row += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9)), -m]
+    x = np.array(row, dtype=np.float32)[None, :]
+    codes, s = O.quantize_act_fp8(x)
+    assert s[0] == np.float32(1.0)
+    assert np.array_equal(codes[0], _e4m3_nearest_by_midpoints(x[0]))
+
+
+def test_fp8_quotients_near_midpoints():
+    """Rows at non-power-of-two absmax whose values put fl32(x/scale) within
+    a few float32 steps of every E4M3 midpoint: the code is decided by the
+    correctly rounded float32 quotient (exact rationals here), which a
+    reciprocal multiply or a quotient kept in float64 gets wrong at some."""
+    vals = [_e4m3_value_exact(c) for c in range(127)]
+    mids = [(a + b) / 2 for a, b in zip(vals[:-1], vals[1:])]
+    for amax in (3.0, 7.25, 0.3, 1e-3, 5.5, 123.4, 0.07):
+        amax32 = np.float32(amax)
+        s_ref = _f32(float(amax32) / 448.0)
+        xs = []
+        for m in mids:
+            c = np.float32(float(m) * s_ref)
+            for _ in range(3):
+                c = np.nextafter(c, np.float32(0))
+            for _ in range(7):
+                if abs(c) <= amax32:
+                    xs += [c, -c]
+                c = np.nextafter(c, np.float32(1e30))
+        x = np.array([amax32] + xs, dtype=np.float32)[None, :]
+        codes, s = O.quantize_act_fp8(x)
+        assert float(s[0]) == s_ref
+        # exact quotient rounded once to binary32 (all quotients here are normal)
+        q32 = np.array([float(_round_binary(Fraction(float(t)) / Fraction(s_ref), 24)) for t in x[0]],
+                       dtype=np.float32)
+        assert np.array_equal(codes[0], _e4m3_nearest_by_midpoints(q32)), amax
+
+
 def test_int4_values_exact_in_e4m3():
     v = np.arange(-8, 8, dtype=np.float32)
     assert np.array_equal(O.e4m3_decode(O.e4m3_encode(v)), v.astype(np.float64))
@@ -580,3 +662,95 @@ def test_asym_epilogue_vs_dequantize_then_matmul():
                 C[n] += (q[k, n] - 8) * float(sc[k // g_eff, n])
         assert np.allclose(O.weight_offsets(O.unpack_gptq_kn(qw), sc, group), C, rtol=1e-12, atol=1e-12)
         assert np.allclose(ref["y"][3], float(x32[3, 0]) * C, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- bf16 rounding and the prefill dequantization
+
+def _round_binary(fr: Fraction, p: int) -> Fraction:
+    """Round an exact rational to p significant bits, nearest even (normal range)."""
+    if fr == 0:
+        return Fraction(0)
+    sgn = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - (p - 1))
+    return sgn * _rne_int(a / ulp) * ulp
+
+
+def test_f32_to_bf16_rounding():
+    """Against exact rational rounding to 8 significant bits and against the
+    library's float32 -> bfloat16 cast, on random values, exact ties of both
+    parities and their float32 neighbours."""
+    import torch
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal(4000) * np.exp2(rng.uniform(-30, 30, 4000))).astype(np.float32)
+    ties = (rng.integers(1, 1 << 16, 500).astype(np.uint32) << 16) | np.uint32(0x8000)
+    t = ties.view(np.float32)
+    v = np.concatenate([v, t, np.nextafter(t, np.float32(0)), np.nextafter(t, np.float32(np.inf)), -t])
+    v = v[np.isfinite(v)]
+    got = O.f32_to_bf16_bits(v)
+    for x, g in zip(v[:1500], got[:1500]):
+        want = _round_binary(Fraction(float(x)), 8)
+        assert Fraction(float(O.bf16_bits_to_f32(np.array([g]))[0])) == want, (float(x), hex(int(g)))
+    lib = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, lib)
+
+
+def test_dequantize_bf16_fixture():
+    """Hand-worked values (tests/golden/dequant_bf16.txt), including ties where
+    the one-rounding reading and op-by-op bf16 rounding differ."""
+    for line in open(os.path.join(GOLD, "dequant_bf16.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        q, sc, z, w = line.split()
+        sb = O.f32_to_bf16_bits(np.array([[float(sc)]], dtype=np.float32))
+        zb = O.f32_to_bf16_bits(np.array([[float(z)]], dtype=np.float32))
+        assert O.bf16_bits_to_f32(sb)[0, 0] == float(sc) and O.bf16_bits_to_f32(zb)[0, 0] == float(z)
+        got = O.dequantize_bf16(np.full((1, 64), int(q), np.uint8), sb, zb, 64)
+        assert np.all(got == int(w, 16)), (line, hex(int(got[0, 0])))
+
+
+def test_dequantize_bf16_exact_rationals():
+    """Random codes, bf16 scales and offsets: the exact value (q - 8)*s + z
+    rounded to float32 and then to bf16, with rationals, per element."""
+    rng = np.random.default_rng(17)
+    N, K, g = 6, 256, 64
+    q = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    sb = O.f32_to_bf16_bits(rng.uniform(0.005, 0.02, (N, K // g)).astype(np.float32))
+    zb = O.f32_to_bf16_bits((rng.standard_normal((N, K // g)) * 0.01).astype(np.float32))
+    got = O.dequantize_bf16(q, sb, zb, g)
+    s = O.bf16_bits_to_f32(sb)
+    z = O.bf16_bits_to_f32(zb)
+    for n in range(N):
+        for k in range(K):
+            ex = (int(q[n, k]) - 8) * Fraction(float(s[n, k // g])) + Fraction(float(z[n, k // g]))
+            want = _round_binary(_round_binary(ex, 24), 8)
+            assert Fraction(float(O.bf16_bits_to_f32(got[n:n + 1, k:k + 1])[0, 0])) == want, (n, k)
+
+
+def test_prefill_reference_reduces_to_exact_w4a16():
+    """With zero offsets and power-of-two scales every dequantized weight is
+    exact in bf16, so the prefill reference equals the exact W4A16 reference
+    (pinned separately); with general scales they differ by at most the bf16
+    rounding of each weight."""
+    rng = np.random.default_rng(23)
+    M, N, K, g = 5, 24, 256, 64
+    xb = O.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    q = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    wb = O.pack_nibble_bytes(q)
+    s_pow2 = O.f32_to_bf16_bits(np.exp2(rng.integers(-9, -5, (N, K // g))).astype(np.float32))
+    z0 = np.zeros((N, K // g), np.uint16)
+    a = O.w4a16_prefill_reference(xb, wb, s_pow2, z0, g)
+    b = O.w4a16_reference(xb, wb, s_pow2, z0, g)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+    sb = O.f32_to_bf16_bits(rng.uniform(0.005, 0.02, (N, K // g)).astype(np.float32))
+    zb = O.f32_to_bf16_bits((rng.standard_normal((N, K // g)) * 0.01).astype(np.float32))
+    a = O.w4a16_prefill_reference(xb, wb, sb, zb, g)
+    b = O.w4a16_reference(xb, wb, sb, zb, g)
+    x = O.bf16_bits_to_f32(xb).astype(np.float64)
+    wexact = O.dequantize_groupwise(q, O.bf16_bits_to_f32(sb), O.bf16_bits_to_f32(zb), g)
+    bound = np.abs(x) @ (np.abs(wexact) * 2.0 ** -8).T
+    assert np.all(np.abs(a - b) <= bound + 1e-12)
+    assert not np.allclose(a, b, rtol=0, atol=1e-9)              # the rounding is really there
