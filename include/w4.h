@@ -155,7 +155,9 @@ int w4a8_weight_offsets(const void* w_tiled, const void* w_scale, int scale_dtyp
  * term joins the bias in its fp32 epilogue).
  *   a_offset   device, fp32 [M];  w_offsets: device, fp32 [N] from
  *              w4a8_weight_offsets for the same weights, scales and group
- *   other arguments, layouts and errors as w4a8_gemm.
+ *   other arguments, layouts and errors as w4a8_gemm, except that the
+ *   largest K-group (K with group -1) is 131071: asymmetric codes reach
+ *   -128, so the int32 sums of 16 * a * (q - 8) need the tighter bound.
  */
 int w4a8_gemm_asym(const int8_t* a, const float* a_scale, const float* a_offset, const void* w_tiled,
                    const void* w_scale, int scale_dtype, int64_t group, const float* w_offsets,
@@ -184,6 +186,23 @@ int w4_repack_bytes(int64_t K, int64_t N, size_t* bytes);
  */
 int w4_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch,
               void* dst, void* stream);
+
+/*
+ * Nibble packing of the byte layout ([cpu_int4] pack_nibbles, unpack_nibbles):
+ * [N, K] codes (0..15, one per byte) <-> [N, K/2] bytes with byte j of a row
+ * holding code 2j in its low nibble and code 2j+1 in its high nibble, the
+ * layout w4a16_repack, w4a16_dequantize and w4_quantize_groupwise use.
+ * w4_unpack_nibbles writes the codes as uint8 (the page returns them in an
+ * int32 tensor; the values are the same).
+ *   codes    device, uint8 [N, K] contiguous; w4_pack_nibbles keeps the low
+ *            nibble of each (codes above 15 are outside the definition)
+ *   packed   device, uint8 [N, K/2] contiguous
+ *   Both buffers 16-byte aligned; the caller owns them.
+ * Errors: INVALID (negative size, null pointer), ALIGN (K odd; pointers),
+ *         UNSUPPORTED (N*K above 2^40), HIP. N == 0 or K == 0 enqueues nothing.
+ */
+int w4_pack_nibbles(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, void* stream);
+int w4_unpack_nibbles(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes, void* stream);
 
 /*
  * W4A8 GEMM with fused dequantization epilogue.
@@ -217,9 +236,11 @@ int w4a8_gemm(const int8_t* a, const float* a_scale, const void* w_tiled,
               int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
- * Test hook of w4a8_gemm: the same kernel writing the exact int32 per-group
- * partial sums P[m, g, n] (layout [M, G, N]) instead of the epilogue.
- * Arguments as w4a8_gemm. Errors as w4a8_gemm.
+ * Test hook of w4a8_gemm: the exact int32 per-group partial sums P[m, g, n]
+ * (layout [M, G, N], G = K/group, 1 for group -1). It launches the kernel
+ * mode w4a8_gemm launches for the same group (the group-128 and per-channel
+ * pipelines included) with a store of each finished group's int32 sum in
+ * place of the scaling epilogue. Arguments as w4a8_gemm. Errors as w4a8_gemm.
  */
 int w4a8_gemm_partials(const int8_t* a, const void* w_tiled, int64_t group,
                        int32_t* partials, int64_t M, int64_t N, int64_t K,

@@ -40,6 +40,7 @@ hipError_t launch_dequantize(const uint8_t* w, const void* scale, const void* ze
                              int64_t K, void* out, hipStream_t stream);
 hipError_t launch_embedding(const int32_t* ids, int64_t T, const void* w_tiled, const void* sz_tiled, int64_t group,
                             int64_t V, int64_t K, void* out, hipStream_t stream);
+hipError_t launch_nibbles(const uint8_t* src, uint8_t* dst, int64_t N, int64_t K, bool pack, hipStream_t stream);
 hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* gsum, const int32_t* row_token,
                               const int32_t* offsets, int64_t E, const void* w_tiled, size_t w_bytes_per_expert,
                               const void* w_scale, int64_t group, void* out, int64_t T, int64_t R, int64_t N,
@@ -174,13 +175,16 @@ int w4_repack(const void* src, int layout, int64_t K, int64_t N, int64_t batch, 
 // The int8 kernels sum 16 * a * (q - 8) over a whole group in int32 (the
 // nibble is unpacked as a byte 16 (q - 8)): |sum| <= 16 * 127 * 8 * group,
 // below 2^31 for groups of at most 132096 (= K for per-channel weights).
+// Asymmetric codes reach -128: |sum| <= 16 * 128 * 8 * group, below 2^31 for
+// groups of at most 131071.
 constexpr int64_t kMaxInt8Group = 132096;
-static int check_int32_range(const char* fn, int64_t group, int64_t K) {
+constexpr int64_t kMaxInt8GroupAsym = 131071;
+static int check_int32_range(const char* fn, int64_t group, int64_t K, int64_t max_group = kMaxInt8Group) {
   const int64_t g = group == -1 ? K : group;
-  if (g > kMaxInt8Group)
+  if (g > max_group)
     return fail(W4_ERR_UNSUPPORTED,
                 "%s: a K-group of %lld exceeds %lld, the largest whose int32 partial sums cannot overflow", fn,
-                (long long)g, (long long)kMaxInt8Group);
+                (long long)g, (long long)max_group);
   return W4_OK;
 }
 
@@ -277,7 +281,9 @@ int w4a8_gemm_asym(const int8_t* a, const float* a_scale, const float* a_offset,
                 fn, scale_dtype);
   if (out_dtype != W4_BF16 && out_dtype != W4_F16)
     return fail(W4_ERR_DTYPE, "%s: output must be bf16 or fp16 (dtype code %d)", fn, out_dtype);
-  int rc = check_gemm(fn, a, w_tiled, group, M, N, K);
+  int rc = check_mnk(fn, M, N, K);
+  if (!rc && (group == -1 || group > 0)) rc = check_int32_range(fn, group, K, kMaxInt8GroupAsym);
+  if (!rc) rc = check_gemm(fn, a, w_tiled, group, M, N, K);
   if (rc) return rc;
   if (M == 0 || N == 0) return ok();
   if (!a_scale || !a_offset || !w_scale || !w_offsets || !out)
@@ -519,6 +525,25 @@ int w4a16_dequantize(const uint8_t* w, const void* scale, const void* zero, int 
   if ((reinterpret_cast<uintptr_t>(w) & 7u) || !aligned16(out))
     return fail(W4_ERR_ALIGN, "%s: w must be 8-byte and out 16-byte aligned", fn);
   return hip_status(w4::launch_dequantize(w, scale, zero, group, N, K, out, static_cast<hipStream_t>(stream)), fn);
+}
+
+static int nibbles(const char* fn, const uint8_t* src, int64_t N, int64_t K, uint8_t* dst, bool pack, void* stream) {
+  if (N < 0 || K < 0) return fail(W4_ERR_INVALID, "%s: negative size N=%lld K=%lld", fn, (long long)N, (long long)K);
+  if (K % 2) return fail(W4_ERR_ALIGN, "%s: K=%lld must be even (two codes per byte)", fn, (long long)K);
+  if (N > kMaxDim || K > ((int64_t)1 << 31) || N * K > ((int64_t)1 << 40))
+    return fail(W4_ERR_UNSUPPORTED, "%s: sizes too large (N=%lld K=%lld)", fn, (long long)N, (long long)K);
+  if (N == 0 || K == 0) return ok();
+  if (!src || !dst) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(src) || !aligned16(dst)) return fail(W4_ERR_ALIGN, "%s: buffers must be 16-byte aligned", fn);
+  return hip_status(w4::launch_nibbles(src, dst, N, K, pack, static_cast<hipStream_t>(stream)), fn);
+}
+
+int w4_pack_nibbles(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, void* stream) {
+  return nibbles("w4_pack_nibbles", codes, N, K, packed, true, stream);
+}
+
+int w4_unpack_nibbles(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes, void* stream) {
+  return nibbles("w4_unpack_nibbles", packed, N, K, codes, false, stream);
 }
 
 }  // extern "C"

@@ -80,3 +80,83 @@ hipError_t launch_repack(const void* src, int layout, int64_t K, int64_t N, int6
 }
 
 }  // namespace w4
+
+namespace w4 {
+
+// [N, K] codes <-> [N, K/2] bytes, byte j = q[2j] | q[2j+1] << 4 (the
+// cpu_int4.py page, pack_nibbles / unpack_nibbles). Rows are contiguous and K
+// is even, so both are flat streams: packed byte j of the whole matrix holds
+// codes 2j and 2j+1 of the whole matrix. A thread takes 16 packed bytes (32
+// codes): one 16-byte load and two 16-byte stores, or the reverse; the last
+// partial chunk goes byte by byte.
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b) {
+  // a, b: four codes each (bytes); result: the 2-byte pairs (a0 a1)(a2 a3)(b0 b1)(b2 b3)
+  const uint32_t ma = a & 0x0F0F0F0Fu, mb = b & 0x0F0F0F0Fu;
+  const uint32_t pa = (ma | (ma >> 4)) & 0x00FF00FFu;     // bytes 0, 2: code 2i | code 2i+1 << 4
+  const uint32_t pb = (mb | (mb >> 4)) & 0x00FF00FFu;
+  return (pa & 0xFFu) | ((pa >> 8) & 0xFF00u) | ((pb & 0xFFu) << 16) | ((pb << 8) & 0xFF000000u);
+}
+
+__device__ __forceinline__ void unpack4(uint32_t p, uint32_t& a, uint32_t& b) {
+  // p: 4 packed bytes -> a: codes of bytes 0, 1; b: codes of bytes 2, 3
+  const uint32_t lo = p & 0x0F0F0F0Fu, hi = (p >> 4) & 0x0F0F0F0Fu;
+  a = (lo & 0xFFu) | ((hi & 0xFFu) << 8) | ((lo & 0xFF00u) << 8) | ((hi & 0xFF00u) << 16);
+  b = ((lo >> 16) & 0xFFu) | ((hi >> 8) & 0xFF00u) | (lo & 0xFF000000u) >> 8 | (hi & 0xFF000000u);
+}
+
+__global__ __launch_bounds__(256) void pack_nibbles_kernel(const uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ packed, int64_t nbytes) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // 16-byte chunk of packed
+  const int64_t b0 = 16 * c;
+  if (b0 >= nbytes) return;
+  if (b0 + 16 <= nbytes) {
+    const v4i x0 = *reinterpret_cast<const v4i*>(codes + 2 * b0);
+    const v4i x1 = *reinterpret_cast<const v4i*>(codes + 2 * b0 + 16);
+    v4i r;
+    r[0] = (int)pack4((uint32_t)x0[0], (uint32_t)x0[1]);
+    r[1] = (int)pack4((uint32_t)x0[2], (uint32_t)x0[3]);
+    r[2] = (int)pack4((uint32_t)x1[0], (uint32_t)x1[1]);
+    r[3] = (int)pack4((uint32_t)x1[2], (uint32_t)x1[3]);
+    *reinterpret_cast<v4i*>(packed + b0) = r;
+  } else {
+    for (int64_t j = b0; j < nbytes; ++j)
+      packed[j] = (uint8_t)((codes[2 * j] & 0xFu) | ((codes[2 * j + 1] & 0xFu) << 4));
+  }
+}
+
+__global__ __launch_bounds__(256) void unpack_nibbles_kernel(const uint8_t* __restrict__ packed,
+                                                             uint8_t* __restrict__ codes, int64_t nbytes) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b0 = 16 * c;
+  if (b0 >= nbytes) return;
+  if (b0 + 16 <= nbytes) {
+    const v4i p = *reinterpret_cast<const v4i*>(packed + b0);
+    v4i r0, r1;
+    uint32_t a, b;
+    unpack4((uint32_t)p[0], a, b); r0[0] = (int)a; r0[1] = (int)b;
+    unpack4((uint32_t)p[1], a, b); r0[2] = (int)a; r0[3] = (int)b;
+    unpack4((uint32_t)p[2], a, b); r1[0] = (int)a; r1[1] = (int)b;
+    unpack4((uint32_t)p[3], a, b); r1[2] = (int)a; r1[3] = (int)b;
+    *reinterpret_cast<v4i*>(codes + 2 * b0) = r0;
+    *reinterpret_cast<v4i*>(codes + 2 * b0 + 16) = r1;
+  } else {
+    for (int64_t j = b0; j < nbytes; ++j) {
+      codes[2 * j] = packed[j] & 0xFu;
+      codes[2 * j + 1] = packed[j] >> 4;
+    }
+  }
+}
+
+hipError_t launch_nibbles(const uint8_t* src, uint8_t* dst, int64_t N, int64_t K, bool pack, hipStream_t stream) {
+  const int64_t nbytes = N * (K / 2);
+  if (nbytes == 0) return hipSuccess;
+  const int64_t chunks = (nbytes + 15) / 16;
+  dim3 grid((unsigned)((chunks + 255) / 256)), block(256);
+  if (pack)
+    hipLaunchKernelGGL(pack_nibbles_kernel, grid, block, 0, stream, src, dst, nbytes);
+  else
+    hipLaunchKernelGGL(unpack_nibbles_kernel, grid, block, 0, stream, src, dst, nbytes);
+  return hipGetLastError();
+}
+
+}  // namespace w4

@@ -197,7 +197,11 @@ hipError_t launch_w4a16_tiled(const void* x, bool f16, const void* w_tiled, cons
   if (M == 0 || N == 0) return hipSuccess;
   const int KT = (int)((K + kTileK - 1) / kTileK), NCG = (int)((N + 15) / 16);
   const int geff = (int)(group == -1 ? K : group);
-  const int cpg = geff == 64 ? 2 : (geff == 128 ? 4 : 8);
+  // A group part (CPG 32-K steps at a multiple of its own length) must lie in
+  // one group, since it is scaled by the group of its first K: parts of 256
+  // when groups are multiples of 256 (or there is one group), of 128 when
+  // they are multiples of 128, else of 64 (groups are multiples of 64).
+  const int cpg = (geff % 256 == 0 || geff >= K) ? 8 : (geff % 128 == 0 ? 4 : 2);
   int rt = (NCG + 255) / 256;
   rt = rt <= 1 ? 1 : (rt == 2 ? 2 : 4);
   const int mv = M == 1 ? 1 : (M == 2 ? 2 : 4);

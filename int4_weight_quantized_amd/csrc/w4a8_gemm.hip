@@ -13,8 +13,9 @@
 //   Group 128 and per-channel: three A-only LDS stages (48 KiB), A two K
 //   steps ahead, B straight into registers (one step ahead for group 128,
 //   two for per-channel, in alternating register sets); two blocks per CU
-//   (three for per-channel at 166 VGPRs). Other group sizes and the partials
-//   hook: two A+B stages (64 KiB), loads one step ahead.
+//   (three for per-channel at 166 VGPRs). Other group sizes: two A+B stages
+//   (64 KiB), loads one step ahead. The int32 partials test hook runs each
+//   of these modes with a store in place of the epilogue.
 // - Loads are raw buffer loads. A (int8 codes) goes straight from memory to
 //   LDS, its range check zero-filling rows past M; B is the tiled int4
 //   layout, 8 KiB contiguous per tile.
@@ -56,7 +57,7 @@ constexpr int kStage = kStageA + kStageB;
 // kModeSplit: group 128 with K split over `splits` blocks per tile; each
 // writes its fp32 partial tile (a_scale applied, no bias) to ws[split][M][N]
 // and w4a8_split_finalize sums them.
-enum { kModeGroup = 0, kModeChannel = 1, kModePartials = 2, kModeSplit = 3 };
+enum { kModeGroup = 0, kModeChannel = 1, kModeSplit = 3 };
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -65,7 +66,12 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // GC: 64-deep chunks per weight group when known at compile time (1: group
 // 64, 2: group 128), 0: taken from group_chunks at run time.
-template <int MODE, bool OUT_BF16, int GC>
+// PART: the test hook's instantiation of the same mode. Where the epilogue
+// would scale a finished group it stores the exact int32 partial sum
+// P[m,g,n] (the accumulator holds 16 P) to partials [M, G, N] instead, and
+// the kernel ends after the K loop; loads, unpack, LDS layout, MFMAs and
+// their schedule are the ones the epilogue-fused instantiation runs.
+template <int MODE, bool OUT_BF16, int GC, bool PART>
 __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
@@ -78,6 +84,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   constexpr bool kPingPong = ((MODE == kModeGroup || MODE == kModeSplit) && GC == 2) || MODE == kModeChannel;
   constexpr bool kStepScales = kPingPong && MODE != kModeChannel;
   static_assert(MODE != kModeSplit || GC == 2, "split K is built for group 128");
+  static_assert(!PART || MODE != kModeSplit, "partials are stored by the unsplit modes");
   // group 128: three A-only stages (B stays in registers); otherwise two A+B stages
   constexpr int kSS = kPingPong ? kStageA : kStage;     // bytes per stage
   constexpr int kNS = kPingPong ? 3 : 2;                // stages
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // fp16 scales of group g for the lane's 4 columns, two per register, at
   // clamped columns: a column past N is never stored
   const __amdgpu_buffer_rsrc_t srsrc =
-      make_rsrc(wscale, (MODE == kModePartials) ? 0u : (uint32_t)((int64_t)G * N * 2));
+      make_rsrc(wscale, PART ? 0u : (uint32_t)((int64_t)G * N * 2));
   uint32_t s_voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) s_voff[j] = 2u * (uint32_t)min(ncol[j], N - 1);
@@ -223,7 +230,8 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // group epilogue for sub-tile rows [I0, I1)
   auto epilogue = [&](auto I0c, auto I1c, const h2 (&raw)[2], int g) {
     constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
-    if constexpr (MODE == kModePartials) {
+    if constexpr (PART) {
+      if (g < 0) return;                                  // the first step's rows 2-3 hold no group yet
 #pragma unroll
       for (int i = I0; i < I1; ++i)
 #pragma unroll
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       // scales of the groups ending in this step (at most two)
       h2 s0[2], s1[2];
       const int cg0 = 2 * tk;
-      if constexpr (MODE == kModeGroup) {
+      if constexpr (MODE == kModeGroup && !PART) {
         fetch_scales(min(cg0 / group_chunks, G - 1), s0);
         fetch_scales(min((cg0 + 1) / group_chunks, G - 1), s1);
       }
@@ -483,7 +491,13 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // (or reuses LDS) with its own DMA in flight
   __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
   if constexpr (kStepScales) epilogue(IC<2>{}, IC<4>{}, scr_prev, kt1 - 1);
-  if constexpr (MODE == kModePartials) return;
+  if constexpr (PART) {
+    if constexpr (MODE == kModeChannel) {                 // one group: all of K
+      const h2 none[2] = {h2{0, 0}, h2{0, 0}};
+      epilogue(IC<0>{}, IC<4>{}, none, 0);
+    }
+    return;
+  }
   if constexpr (MODE == kModeSplit) {
     // fp32 partial tile with the row scale applied: rows of 16 columns are
     // 64-byte runs per store instruction
@@ -577,19 +591,23 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
   auto B = static_cast<const uint16_t*>(bias);
   auto O = static_cast<uint16_t*>(out);
   const int iM = (int)M, iN = (int)N, iK = (int)K;
-#define W4A8_LAUNCH(MODE_, BF16_, GC_)                                                                  \
-  hipLaunchKernelGGL((w4a8_gemm_kernel<MODE_, BF16_, GC_>), grid, block, 0, stream, a, a_scale, W, S, gc, B, O, \
-                     partials, iM, iN, iK, KT, tilesM, tilesN, nullptr, 1, a_off, w_off)
+#define W4A8_LAUNCH(MODE_, BF16_, GC_, PART_)                                                          \
+  hipLaunchKernelGGL((w4a8_gemm_kernel<MODE_, BF16_, GC_, PART_>), grid, block, 0, stream, a, a_scale, W, S, gc, \
+                     B, O, partials, iM, iN, iK, KT, tilesM, tilesN, nullptr, 1, a_off, w_off)
+  // the partials hook takes the same mode and chunk count as the GEMM
   if (partials) {
-    W4A8_LAUNCH(kModePartials, true, 0);
+    if (group == -1) W4A8_LAUNCH(kModeChannel, true, 0, true);
+    else if (gc == 1) W4A8_LAUNCH(kModeGroup, true, 1, true);
+    else if (gc == 2) W4A8_LAUNCH(kModeGroup, true, 2, true);
+    else W4A8_LAUNCH(kModeGroup, true, 0, true);
   } else if (group == -1) {
-    if (out_bf16) W4A8_LAUNCH(kModeChannel, true, 0); else W4A8_LAUNCH(kModeChannel, false, 0);
+    if (out_bf16) W4A8_LAUNCH(kModeChannel, true, 0, false); else W4A8_LAUNCH(kModeChannel, false, 0, false);
   } else if (gc == 1) {
-    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 1); else W4A8_LAUNCH(kModeGroup, false, 1);
+    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 1, false); else W4A8_LAUNCH(kModeGroup, false, 1, false);
   } else if (gc == 2) {
-    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 2); else W4A8_LAUNCH(kModeGroup, false, 2);
+    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 2, false); else W4A8_LAUNCH(kModeGroup, false, 2, false);
   } else {
-    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 0); else W4A8_LAUNCH(kModeGroup, false, 0);
+    if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 0, false); else W4A8_LAUNCH(kModeGroup, false, 0, false);
   }
 #undef W4A8_LAUNCH
   return hipGetLastError();
@@ -700,7 +718,7 @@ hipError_t launch_w4a8_gemm_split(const int8_t* a, const float* a_scale, const v
   const int KT = (int)((K + kBK - 1) / kBK);
   const int tilesM = (int)((M + kBM - 1) / kBM), tilesN = (int)((N + kBN - 1) / kBN);
   dim3 grid((unsigned)(tilesM * tilesN * splits)), block(kGThreads);
-  hipLaunchKernelGGL((w4a8_gemm_kernel<kModeSplit, true, 2>), grid, block, 0, stream, a, a_scale,
+  hipLaunchKernelGGL((w4a8_gemm_kernel<kModeSplit, true, 2, false>), grid, block, 0, stream, a, a_scale,
                      static_cast<const v4i*>(w_tiled), static_cast<const uint16_t*>(w_scale), 2,
                      static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(nullptr), nullptr, (int)M, (int)N,
                      (int)K, KT, tilesM, tilesN, ws, splits, nullptr, nullptr);

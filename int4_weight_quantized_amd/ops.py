@@ -42,6 +42,8 @@ _SIGS = {
     "w4a8_quantize_act_asym": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P],
     "w4a8_weight_offsets": [_P, _P, _I, _I64, _I64, _I64, _P, _P],
     "w4a8_gemm_asym": [_P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _I, _I64, _I64, _I64, _P],
+    "w4_pack_nibbles": [_P, _I64, _I64, _P, _P],
+    "w4_unpack_nibbles": [_P, _I64, _I64, _P, _P],
     "w4_last_error": [],
     "w4_version": [],
 }
@@ -189,6 +191,24 @@ def w4_repack(src: torch.Tensor, layout: int, K: int, N: int, batch: int = 1, st
     dst = torch.empty((batch, nbytes), dtype=torch.uint8, device=src.device)
     _check("w4_repack", lib().w4_repack(_ptr(src), layout, K, N, batch, _ptr(dst), _stream(stream)))
     return dst
+
+
+def w4_pack_nibbles(codes: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """codes uint8 [N, K] (0..15) -> uint8 [N, K/2], low nibble first."""
+    N, K = codes.shape
+    if out is None:
+        out = torch.empty((N, K // 2), dtype=torch.uint8, device=codes.device)
+    _check("w4_pack_nibbles", lib().w4_pack_nibbles(_ptr(codes), N, K, _ptr(out), _stream(stream)))
+    return out
+
+
+def w4_unpack_nibbles(packed: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """uint8 [N, K/2] -> codes uint8 [N, K]."""
+    N, K = packed.shape[0], packed.shape[1] * 2
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.uint8, device=packed.device)
+    _check("w4_unpack_nibbles", lib().w4_unpack_nibbles(_ptr(packed), N, K, _ptr(out), _stream(stream)))
+    return out
 
 
 def w4a8_gemm(a, a_scale, w_tiled, w_scale, group: int, N: int, out_dtype=torch.bfloat16, bias=None,

@@ -150,6 +150,8 @@ EDGE_SHAPES = [  # (M, K, N, group)
     (1, 64, 8, -1), (5, 8, 8, -1), (130, 200, 24, -1), (33, 192, 136, 64),
     (17, 512, 256, 256), (129, 384, 264, 128), (64, 1024, 512, 128), (3, 14336, 16, -1),
     (9, 384, 40, -1), (67, 640, 136, -1), (200, 1408, 264, -1),
+    # groups of an odd number of 64-deep chunks: group boundaries fall inside K steps
+    (40, 576, 136, 192), (70, 1152, 264, 384), (9, 960, 40, 320), (131, 1920, 136, 640),
 ]
 
 
@@ -230,6 +232,20 @@ def test_repack_layouts_agree():
     assert np.array_equal(P.cpu().numpy().astype(np.int64), Pref)
 
 
+@pytest.mark.parametrize("N,K", [(1, 2), (3, 30), (16, 64), (37, 1030), (1000, 4096), (5, 8)])
+def test_nibble_pack_unpack(N, K):
+    """w4_pack_nibbles / w4_unpack_nibbles bit-exact against the oracle's byte
+    layout (flat 16-byte chunks plus a byte-wise tail)."""
+    rng = np.random.default_rng(N * 31 + K)
+    q = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    packed = ops.w4_pack_nibbles(torch.from_numpy(q).to(DEV))
+    assert np.array_equal(packed.cpu().numpy(), O.pack_nibble_bytes(q))
+    b = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    codes = ops.w4_unpack_nibbles(torch.from_numpy(b).to(DEV))
+    assert np.array_equal(codes.cpu().numpy(), O.unpack_nibble_bytes(b))
+    assert torch.equal(ops.w4_unpack_nibbles(packed), torch.from_numpy(q).to(DEV))
+
+
 # ------------------------------------------------------------------ W4A16 decode
 
 def _w4a16_run(d, with_zero=True):
@@ -299,10 +315,14 @@ def test_grouped_moe_workload():
     off = d["expert_offsets"]
     rng = np.random.default_rng(3)
     rows = []
-    for e in rng.choice(d["E"], 3, replace=False):           # a few experts, first/last/random rows
+    for e in range(d["E"]):                                  # every expert: its first and last row, two more
         lo, hi = int(off[e]), int(off[e + 1])
-        rows += [lo, hi - 1] + list(rng.integers(lo, hi, 6))
+        if hi > lo:
+            rows += [lo, hi - 1] + list(rng.integers(lo, hi, 2))
+    last = max(e for e in range(d["E"]) if off[e + 1] > off[e])
+    rows += list(range(int(off[last]), int(off[last + 1])))  # every row of the last expert (ragged last tile)
     rows = np.unique(np.array(rows))
+    print(f"[moe] checking {rows.size} routed rows of {int(off[-1])}", flush=True)
     ref = O.grouped_fp8_reference(rc, rs, d["row_token"], off, d["w"], d["scales"], d["group"], rows=rows)
     assert_close(to_f64(y[torch.from_numpy(rows).to(DEV)]), ref, "moe sample")
     assert torch.isfinite(y.float()).all()
@@ -320,7 +340,10 @@ def _tiled_weights(d):
     (1, 4096, 14336, 128, "bf16", False), (8, 4096, 14336, 128, "bf16", True), (16, 256, 256, 128, "bf16", False),
     (3, 192, 24, 64, "f16", True), (5, 1024, 264, -1, "bf16", False), (1, 8192, 136, 512, "f16", False),
     (13, 14336, 72, 256, "bf16", True), (2, 200, 40, -1, "f16", False), (16, 4096, 1000, 64, "f16", True),
-    (4, 4352, 4104, 128, "bf16", False)])
+    (4, 4352, 4104, 128, "bf16", False),
+    # groups that do not divide a wave's 256-K range: group boundaries inside it
+    (3, 768, 136, 384, "bf16", True), (5, 1152, 264, 192, "f16", False), (1, 1920, 40, 320, "bf16", False),
+    (7, 2560, 72, 640, "bf16", True), (16, 4608, 520, 1152, "f16", False), (2, 3072, 264, 768, "bf16", True)])
 def test_w4a16_tiled(M, K, N, group, dtype, bias):
     d = W.w4a8_inputs(M, K, N, group, dtype, seed=7 * M + K + N, with_bias=bias)
     print(f"\n[w4a16 tiled] M={M} K={K} N={N} g={group} {dtype} bias={bias}", flush=True)
@@ -333,15 +356,17 @@ def test_w4a16_tiled(M, K, N, group, dtype, bias):
     assert_close(to_f64(y), ref, f"w4a16 tiled {M}x{K}x{N} g{group} {dtype}")
 
 
-@pytest.mark.parametrize("M,threshold,group,dtype", [
-    (20, 32, 128, "bf16"), (20, 8, 128, "bf16"), (1, 0, 128, "bf16"), (40, 0, 128, "f16"), (40, 0, 64, "bf16"),
-    (300, 0, 128, "bf16"), (33, 0, -1, "f16")])
-def test_w4_linear_dispatch(M, threshold, group, dtype):
+@pytest.mark.parametrize("M,threshold,group,dtype,K", [
+    (20, 32, 128, "bf16", 1024), (20, 8, 128, "bf16", 1024), (1, 0, 128, "bf16", 1024), (40, 0, 128, "f16", 1024),
+    (40, 0, 64, "bf16", 1024), (300, 0, 128, "bf16", 1024), (33, 0, -1, "f16", 1024),
+    # groups 192 and 384 on both sides of the threshold
+    (20, 0, 192, "bf16", 1152), (40, 0, 192, "f16", 1152), (9, 0, 384, "f16", 1152), (70, 0, 384, "bf16", 1152)])
+def test_w4_linear_dispatch(M, threshold, group, dtype, K):
     """Both sides of the per-call dispatch on the same tiled weights: the
     weight-only path (16 rows per launch) below the threshold, per-token int8
     quantization + W4A8 GEMM from it up (group 128 with few tiles splits K:
     fp32 partial tiles summed by a second kernel)."""
-    K, N = 1024, 520
+    N = 520
     d = W.w4a8_inputs(M, K, N, group, dtype, seed=M + 101 * threshold, with_bias=True)
     print(f"\n[w4_linear] M={M} threshold={threshold} group={group} {dtype}", flush=True)
     wt, sc = _tiled_weights(d)

@@ -31,7 +31,9 @@ def close(gpu: torch.Tensor, y64: np.ndarray) -> bool:
 
 @st.composite
 def w4a8_shapes(draw):
-    group = draw(st.sampled_from([-1, 64, 128, 256]))
+    # 192 and 384: groups that do not divide 256 (a 64- or 128-deep part of
+    # a 256-K range can fall in either of two groups)
+    group = draw(st.sampled_from([-1, 64, 128, 192, 256, 384]))
     kmul = 64 if group == -1 else group
     K = kmul * draw(st.integers(1, 4)) if group != -1 else 8 * draw(st.integers(1, 80))
     N = 8 * draw(st.integers(1, 40))

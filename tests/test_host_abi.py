@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
                  "w4_repack_bytes", "w4a8_gemm_partials", "w4a16_tiled_gemm", "w4_linear", "w4_linear_workspace_bytes",
                  "w4_quantize_groupwise", "w4a16_embedding", "w4a8_quantize_act_static", "w4a16_dequantize",
                  "w4a8_quantize_act_asym", "w4a8_weight_offsets", "w4a8_gemm_asym",
-                 "w4_last_error", "w4_version"):
+                 "w4_pack_nibbles", "w4_unpack_nibbles", "w4_last_error", "w4_version"):
         assert must in names
 
 
@@ -163,3 +163,25 @@ def test_asym_entry_points_validate(L):
     assert L.w4a8_gemm_asym(None, None, None, None, None, 1, 128, None, None, None, 1, 16, 256, 256, None) == -4
     assert L.w4a8_gemm_asym(None, None, None, None, None, 2, 96, None, None, None, 1, 16, 256, 288, None) == -3
     assert L.w4a8_gemm_asym(None, None, None, None, None, 2, 128, None, None, None, 1, 0, 256, 256, None) == 0
+
+
+def test_asym_int32_group_limit(L):
+    """Asymmetric codes reach -128, so the asymmetric GEMM's largest K-group
+    is 131071 (16 * 128 * 8 * g < 2^31), below the symmetric 132096."""
+    K_bad = 131072
+    assert L.w4a8_gemm_asym(None, None, None, None, None, 2, -1, None, None, None, 1, 16, 256, K_bad, None) == -5
+    assert b"131071" in L.w4_last_error()
+    assert L.w4a8_gemm_asym(None, None, None, None, None, 2, -1, None, None, None, 1, 16, 256, K_bad - 8, None) == -1
+    # the symmetric GEMM still takes that K
+    assert L.w4a8_gemm(None, None, None, None, 2, -1, None, None, 1, 16, 256, K_bad, None) == -1
+
+
+def test_nibble_entry_points_validate(L):
+    p = ctypes.c_void_p
+    for fn in (L.w4_pack_nibbles, L.w4_unpack_nibbles):
+        assert fn(p(256), 4, 7, p(256), None) == -2                  # K odd
+        assert fn(p(256), -1, 8, p(256), None) == -1                 # negative
+        assert fn(None, 4, 8, p(256), None) == -1                    # null
+        assert fn(p(256 + 8), 4, 8, p(256), None) == -2              # misaligned
+        assert fn(None, 0, 8, None, None) == 0 and fn(None, 4, 0, None, None) == 0   # empty
+        assert fn(p(256), 1 << 30, 1 << 12, p(256), None) == -5      # too large
