@@ -15,7 +15,8 @@
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device pointers; the caller allocates
  *     and owns every buffer. The library allocates nothing and keeps no state
- *     but the per-thread error message.
+ *     but the per-thread error message (and, for w4_linear_noalloc only, one
+ *     device scratch array per GPU with its looked-up address).
  *   - `stream` is a hipStream_t (NULL: the default stream). Work is enqueued
  *     on it; no entry point synchronizes.
  *   - Arguments are validated before anything is enqueued. On failure the
@@ -352,6 +353,30 @@ int w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group, in
 int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_scale, int scale_dtype,
               int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
               int64_t min_tokens_int8, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same dispatch and kernels, with the workspace taken from a device array
+ * inside the library instead of an argument.
+ *   - The array holds W4_LINEAR_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU
+ *     the entry point runs on, from its first call there until the process
+ *     ends. A call whose workspace (w4_linear_workspace_bytes) exceeds it
+ *     returns W4_ERR_UNSUPPORTED before anything is enqueued; the weight-only
+ *     side (M below the threshold) needs none.
+ *   - Call it with the stream's device current. Its first call on a device
+ *     looks up the array's address there (hipGetSymbolAddress); no call
+ *     allocates (no hipMalloc, hipFree or allocating library routine).
+ *   - Every call on one GPU shares that GPU's array, and the array keeps the
+ *     last call's contents: calls that overlap on one GPU (other streams,
+ *     other threads) race and give undefined results. Nothing in it needs to
+ *     start at zero (each call writes all of the scratch it reads).
+ * Arguments, results and other errors as w4_linear without the workspace.
+ */
+#define W4_LINEAR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int w4_linear_noalloc(const void* x, int x_dtype, const void* w_tiled, const void* w_scale, int scale_dtype,
+                      int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
+                      int64_t min_tokens_int8, void* stream);
 
 /*
  * Prefill path of the W4A16 layer: the weight unpacked to bf16 once per call

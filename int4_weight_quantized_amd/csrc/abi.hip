@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/w4.h"
 #include "w4_device.h"
@@ -434,10 +435,78 @@ int w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group, in
   return ok();
 }
 
+static int linear_impl(const char* fn, const void* x, int x_dtype, const void* w_tiled, const void* w_scale,
+                       int scale_dtype, int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
+                       int64_t min_tokens_int8, void* workspace, size_t workspace_bytes, void* stream);
+
 int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_scale, int scale_dtype, int64_t group,
               const void* bias, void* out, int64_t M, int64_t N, int64_t K, int64_t min_tokens_int8, void* workspace,
               size_t workspace_bytes, void* stream) {
-  const char* fn = "w4_linear";
+  return linear_impl("w4_linear", x, x_dtype, w_tiled, w_scale, scale_dtype, group, bias, out, M, N, K,
+                     min_tokens_int8, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- w4_linear_noalloc: the workspace of w4_linear in a file-scope device
+// array. Its address differs per GPU; it is looked up once per device (with
+// that device current) and kept. Host code never passes the array's name to
+// a kernel: the name is a host-side stand-in, not a device address.
+namespace {
+constexpr size_t kNoAllocScratchBytes = W4_LINEAR_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(const char* fn, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W4_ERR_HIP, "%s: hipGetDevice: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(W4_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(W4_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: HIP error %d (%s)", fn, dev, (int)e,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return W4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int w4_linear_noalloc(const void* x, int x_dtype, const void* w_tiled, const void* w_scale, int scale_dtype,
+                      int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
+                      int64_t min_tokens_int8, void* stream) {
+  const char* fn = "w4_linear_noalloc";
+  int rc = check_tiled(fn, x, x_dtype, w_tiled, w_scale, scale_dtype, group, M, N, K);
+  if (rc) return rc;
+  rc = check_int32_range(fn, group, K);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return ok();
+  const size_t need = linear_workspace(M, N, K, group, min_tokens_int8).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(W4_ERR_UNSUPPORTED, "%s: M=%lld N=%lld K=%lld needs %zu bytes of scratch, above its %zu-byte maximum",
+                fn, (long long)M, (long long)N, (long long)K, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need) {
+    rc = scratch_of_current_device(fn, &ws);
+    if (rc) return rc;
+  }
+  return linear_impl(fn, x, x_dtype, w_tiled, w_scale, scale_dtype, group, bias, out, M, N, K, min_tokens_int8, ws,
+                     need ? kNoAllocScratchBytes : 0, stream);
+}
+
+}  // extern "C"
+
+static int linear_impl(const char* fn, const void* x, int x_dtype, const void* w_tiled, const void* w_scale,
+                       int scale_dtype, int64_t group, const void* bias, void* out, int64_t M, int64_t N, int64_t K,
+                       int64_t min_tokens_int8, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_tiled(fn, x, x_dtype, w_tiled, w_scale, scale_dtype, group, M, N, K);
   if (rc) return rc;
   rc = check_int32_range(fn, group, K);
@@ -476,6 +545,8 @@ int w4_linear(const void* x, int x_dtype, const void* w_tiled, const void* w_sca
   return hip_status(w4::launch_w4a8_gemm(codes, scales, w_tiled, w_scale, group, bias, out, !f16, nullptr, M, N, K, st),
                     fn);
 }
+
+extern "C" {
 
 int w4_quantize_groupwise(const void* w, int w_dtype, int64_t N, int64_t K, int64_t group, uint8_t* packed,
                           void* scale, void* zero, int sz_dtype, void* stream) {

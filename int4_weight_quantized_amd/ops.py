@@ -36,6 +36,7 @@ _SIGS = {
     "w4a16_tiled_gemm": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _P],
     "w4_linear_workspace_bytes": [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "w4_linear": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
+    "w4_linear_noalloc": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _I64, _P],
     "w4a16_dequantize": [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
     "w4_quantize_groupwise": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P],
     "w4a16_embedding": [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P],
@@ -305,6 +306,21 @@ def w4_linear(x, w_tiled, w_scale, group: int, N: int, bias=None, min_tokens_int
         _ptr(x), _half_code(x.dtype), _ptr(w_tiled), _ptr(w_scale), W4_F16 if w_scale.dtype == torch.float16 else W4_BF16,
         group, _ptr(bias), _ptr(out), M, N, K, min_tokens_int8, _ptr(workspace) if need else None,
         workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+W4_LINEAR_NOALLOC_SCRATCH_BYTES = 64 << 20     # include/w4.h
+
+
+def w4_linear_noalloc(x, w_tiled, w_scale, group: int, N: int, bias=None, min_tokens_int8: int = 0, out=None,
+                      stream=None):
+    """w4_linear with the library's own device scratch (no workspace argument)."""
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check("w4_linear_noalloc", lib().w4_linear_noalloc(
+        _ptr(x), _half_code(x.dtype), _ptr(w_tiled), _ptr(w_scale), W4_F16, group, _ptr(bias), _ptr(out), M, N, K,
+        min_tokens_int8, _stream(stream)))
     return out
 
 

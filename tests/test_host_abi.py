@@ -185,3 +185,13 @@ def test_nibble_entry_points_validate(L):
         assert fn(p(256 + 8), 4, 8, p(256), None) == -2              # misaligned
         assert fn(None, 0, 8, None, None) == 0 and fn(None, 4, 0, None, None) == 0   # empty
         assert fn(p(256), 1 << 30, 1 << 12, p(256), None) == -5      # too large
+
+
+def test_noalloc_scratch_limit(L):
+    """w4_linear_noalloc refuses, on the host and before any HIP call, a call
+    whose workspace exceeds its 64 MiB scratch array; M == 0 is a no-op."""
+    p = ctypes.c_void_p
+    rc = L.w4_linear_noalloc(p(256), 1, p(256), p(256), 2, 128, None, p(256), 8192, 256, 8192, 0, None)
+    assert rc == -5 and "scratch" in _err(L)
+    assert L.w4_linear_noalloc(p(256), 1, p(256), p(256), 1, 128, None, p(256), 64, 256, 4096, 0, None) == -4
+    assert L.w4_linear_noalloc(None, 1, None, None, 2, 128, None, None, 0, 256, 4096, 0, None) == 0
