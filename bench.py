@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP8_TFLOPS = 5000.0    # dense fp8 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # HBM3E 8 TB/s
 
 
@@ -282,13 +283,19 @@ def main():
         wdq = torch.empty((Np, Kp), dtype=torch.bfloat16, device=dev)
         yp = torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)
         f_dq = lambda: ops.w4a16_dequantize(wb, sp, zp, gp, out=wdq)
-        f_mm = lambda: torch.matmul(xp, wdq.t(), out=yp)
+        f_mm = lambda: ops.w4a16_prefill_gemm(xp, wdq, out=yp)          # the library's bf16 GEMM
+        f_blas = lambda: torch.matmul(xp, wdq.t(), out=yp)              # baseline: the platform GEMM (hipBLASLt)
         (t_dq, t_mm), t_pf, _ = timed([f_dq, f_mm], max(4, args.steps // 5), max(2, args.warmup // 2))
+        (t_blas,), _, _ = timed([f_blas], max(4, args.steps // 5), max(2, args.warmup // 2))
         dq_bytes = Np * Kp // 2 + 2 * 2 * Np * (Kp // gp) + 2 * Np * Kp
+        fl = 2.0 * Mp * Np * Kp
         prefill = {"workload": f"w4a16 prefill M={Mp} K={Kp} N={Np} group={gp} bf16 (dequantize + bf16 GEMM)",
                    "dequantize_us": t_dq * 1e3, "dequantize_gbs": dq_bytes / (t_dq * 1e-3) / 1e9,
-                   "gemm_us": t_mm * 1e3, "step_us": t_pf * 1e3,
-                   "step_tflops": 2.0 * Mp * Np * Kp / (t_pf * 1e-3) / 1e12}
+                   "gemm_us": t_mm * 1e3, "gemm_tflops": fl / (t_mm * 1e-3) / 1e12,
+                   "gemm_frac_bf16_peak": fl / (t_mm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                   "step_us": t_pf * 1e3, "step_tflops": fl / (t_pf * 1e-3) / 1e12,
+                   "baseline_hipblaslt_gemm_us": t_blas * 1e3,
+                   "baseline_hipblaslt_gemm_tflops": fl / (t_blas * 1e-3) / 1e12}
         del wdq, yp
 
     # ------------------------------------------------------------ MoE grouped

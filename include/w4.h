@@ -389,12 +389,39 @@ int w4_linear_noalloc(const void* x, int x_dtype, const void* w_tiled, const voi
  *   group    64, 128, 256 or 512, dividing K
  *   out      device, bf16 [N, K] row-major (16-byte aligned): computed in
  *            fp32 as fma(q - 8, scale, zero), rounded to nearest even
- * The GEMM itself (x [M, K] times out^T) is the platform's ordinary bf16 GEMM
- * (hipBLASLt), not part of this library.
+ * The GEMM on it is w4a16_prefill_gemm (w4a16_prefill runs both).
  * Errors: INVALID, ALIGN, GROUP, DTYPE, UNSUPPORTED (N*K >= 2^31), HIP.
  */
 int w4a16_dequantize(const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group,
                      int64_t K, int64_t N, void* out, void* stream);
+
+/*
+ * The prefill path's GEMM and the whole path ([cpu_int4] _cpu_int4_linear:
+ * batches at or above the threshold take the dequantized bf16 weight through
+ * an ordinary GEMM, y = x @ w^T).
+ * w4a16_prefill_gemm: hand-written bf16 matrix-core GEMM, fp32 sums, output
+ *   rounded to bf16 (nearest even):
+ *     out[m, n] = sum_k x[m, k] * w[n, k]
+ *   x      device, bf16 [M, K] row-major
+ *   w      device, bf16 [N, K] row-major (e.g. from w4a16_dequantize)
+ *   out    device, bf16 [M, N] row-major
+ *   All three 16-byte aligned; K a multiple of 64, N of 8.
+ * w4a16_prefill_workspace_bytes: N * K * 2, the bf16 weight's size.
+ * w4a16_prefill: w4a16_dequantize into the workspace, then
+ *   w4a16_prefill_gemm, on one stream.
+ *   w, scale, zero, group as w4a16_dequantize; x, out as w4a16_prefill_gemm
+ *   workspace  device, >= w4a16_prefill_workspace_bytes(N, K), 16-byte
+ *              aligned, owned by the caller; calls sharing it must not overlap
+ * Errors: INVALID (null, negative sizes, workspace too small), ALIGN (K % 64,
+ *         N % 8, pointers), GROUP, DTYPE (scale/zero not bf16), UNSUPPORTED
+ *         (sizes; N*K >= 2^31 for w4a16_prefill), HIP. M == 0 or N == 0
+ *         enqueues nothing.
+ */
+int w4a16_prefill_gemm(const void* x, const void* w, void* out, int64_t M, int64_t N, int64_t K, void* stream);
+int w4a16_prefill_workspace_bytes(int64_t N, int64_t K, size_t* bytes);
+int w4a16_prefill(const void* x, const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group,
+                  void* out, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /*
  * Groupwise min/max int4 quantization of a weight matrix, on the device.

@@ -41,6 +41,8 @@ hipError_t launch_dequantize(const uint8_t* w, const void* scale, const void* ze
                              int64_t K, void* out, hipStream_t stream);
 hipError_t launch_embedding(const int32_t* ids, int64_t T, const void* w_tiled, const void* sz_tiled, int64_t group,
                             int64_t V, int64_t K, void* out, hipStream_t stream);
+hipError_t launch_bf16_gemm_nt(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                               hipStream_t stream);
 hipError_t launch_nibbles(const uint8_t* src, uint8_t* dst, int64_t N, int64_t K, bool pack, hipStream_t stream);
 hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* gsum, const int32_t* row_token,
                               const int32_t* offsets, int64_t E, const void* w_tiled, size_t w_bytes_per_expert,
@@ -596,6 +598,59 @@ int w4a16_dequantize(const uint8_t* w, const void* scale, const void* zero, int 
   if ((reinterpret_cast<uintptr_t>(w) & 7u) || !aligned16(out))
     return fail(W4_ERR_ALIGN, "%s: w must be 8-byte and out 16-byte aligned", fn);
   return hip_status(w4::launch_dequantize(w, scale, zero, group, N, K, out, static_cast<hipStream_t>(stream)), fn);
+}
+
+static int check_prefill_gemm(const char* fn, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0)
+    return fail(W4_ERR_INVALID, "%s: sizes must be M >= 0, N >= 0, K > 0 (got M=%lld N=%lld K=%lld)", fn,
+                (long long)M, (long long)N, (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > ((int64_t)1 << 22))
+    return fail(W4_ERR_UNSUPPORTED, "%s: sizes too large (M=%lld N=%lld K=%lld)", fn, (long long)M, (long long)N,
+                (long long)K);
+  if (K % 64 || N % 8)
+    return fail(W4_ERR_ALIGN, "%s: K=%lld must be a multiple of 64 and N=%lld of 8", fn, (long long)K, (long long)N);
+  return W4_OK;
+}
+
+int w4a16_prefill_gemm(const void* x, const void* w, void* out, int64_t M, int64_t N, int64_t K, void* stream) {
+  const char* fn = "w4a16_prefill_gemm";
+  int rc = check_prefill_gemm(fn, M, N, K);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return ok();
+  if (!x || !w || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out))
+    return fail(W4_ERR_ALIGN, "%s: x, w and out must be 16-byte aligned", fn);
+  return hip_status(w4::launch_bf16_gemm_nt(x, w, out, M, N, K, static_cast<hipStream_t>(stream)), fn);
+}
+
+int w4a16_prefill_workspace_bytes(int64_t N, int64_t K, size_t* bytes) {
+  const char* fn = "w4a16_prefill_workspace_bytes";
+  if (!bytes) return fail(W4_ERR_INVALID, "%s: null output pointer", fn);
+  if (N < 0 || K <= 0) return fail(W4_ERR_INVALID, "%s: sizes must be N >= 0, K > 0", fn);
+  *bytes = (size_t)N * (size_t)K * 2;
+  return ok();
+}
+
+int w4a16_prefill(const void* x, const uint8_t* w, const void* scale, const void* zero, int sz_dtype, int64_t group,
+                  void* out, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  const char* fn = "w4a16_prefill";
+  if (sz_dtype != W4_BF16) return fail(W4_ERR_DTYPE, "%s: scale and zero must be bf16 (dtype code %d)", fn, sz_dtype);
+  int rc = check_w4a16(fn, group, N, K);
+  if (!rc) rc = check_prefill_gemm(fn, M, N, K);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return ok();
+  if (!x || !w || !scale || !out) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  const size_t need = (size_t)N * (size_t)K * 2;
+  if (!workspace || workspace_bytes < need)
+    return fail(W4_ERR_INVALID, "%s: workspace of %zu bytes is smaller than the %zu needed for N=%lld K=%lld", fn,
+                workspace_bytes, need, (long long)N, (long long)K);
+  if ((reinterpret_cast<uintptr_t>(w) & 7u) || !aligned16(x) || !aligned16(out) || !aligned16(workspace))
+    return fail(W4_ERR_ALIGN, "%s: w must be 8-byte and x, out, workspace 16-byte aligned", fn);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(w4::launch_dequantize(w, scale, zero, group, N, K, workspace, st), fn);
+  if (rc) return rc;
+  return hip_status(w4::launch_bf16_gemm_nt(x, workspace, out, M, N, K, st), fn);
 }
 
 static int nibbles(const char* fn, const uint8_t* src, int64_t N, int64_t K, uint8_t* dst, bool pack, void* stream) {

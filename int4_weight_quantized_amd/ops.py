@@ -38,6 +38,9 @@ _SIGS = {
     "w4_linear": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
     "w4_linear_noalloc": [_P, _I, _P, _P, _I, _I64, _P, _P, _I64, _I64, _I64, _I64, _P],
     "w4a16_dequantize": [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P],
+    "w4a16_prefill_gemm": [_P, _P, _P, _I64, _I64, _I64, _P],
+    "w4a16_prefill_workspace_bytes": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+    "w4a16_prefill": [_P, _P, _P, _P, _I, _I64, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
     "w4_quantize_groupwise": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P],
     "w4a16_embedding": [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P],
     "w4a8_quantize_act_asym": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P],
@@ -359,3 +362,35 @@ def w4a16_embedding(ids, w_tiled, sz_tiled, group: int, V: int, K: int, out=None
 
 def w4_version() -> int:
     return lib().w4_version()
+
+
+def w4a16_prefill_gemm(x, w, out=None, stream=None):
+    """bf16 x [M, K] times bf16 w [N, K] transposed -> bf16 [M, N]."""
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check("w4a16_prefill_gemm", lib().w4a16_prefill_gemm(_ptr(x), _ptr(w), _ptr(out), M, N, K, _stream(stream)))
+    return out
+
+
+def w4a16_prefill_workspace_bytes(N: int, K: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("w4a16_prefill_workspace_bytes", lib().w4a16_prefill_workspace_bytes(N, K, ctypes.byref(n)))
+    return n.value
+
+
+def w4a16_prefill(x, w, scale, zero, group: int, out=None, workspace=None, stream=None):
+    """The W4A16 prefill path: dequantize the byte-layout weights [N, K/2] to bf16 (in the workspace) and
+    run the bf16 GEMM. The workspace (uint8, device) is allocated here if not given."""
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    need = w4a16_prefill_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    _check("w4a16_prefill", lib().w4a16_prefill(
+        _ptr(x), _ptr(w), _ptr(scale), _ptr(zero), _half_code(scale.dtype), group, _ptr(out), M, N, K,
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

@@ -29,6 +29,7 @@ SEEDS = {
     "w4a8_down_proj": 1003,
     "w4a16_decode": 1004,
     "w4afp8_moe": 1005,
+    "w4a16_prefill": 1006,
 }
 
 SHAPES = {
@@ -37,6 +38,8 @@ SHAPES = {
     "w4a8_down_proj": dict(M=8192, K=14336, N=4096, group=-1, x_dtype="f16"),
     "w4a16_decode": dict(M=8, K=4096, N=14336, group=64, x_dtype="bf16"),
     "w4afp8_moe": dict(E=64, K=7168, N=2048, group=128, T=8192, topk=8, x_dtype="bf16"),
+    # the decode layer's weights at a prefill batch (the asymmetric grid's large-batch path)
+    "w4a16_prefill": dict(M=4096, K=4096, N=14336, group=64, x_dtype="bf16"),
 }
 
 
@@ -153,7 +156,7 @@ def named(name: str, **override) -> dict:
     if name == "w4a8_down_proj":
         return w4a8_inputs(shp["M"], shp["K"], shp["N"], shp["group"], shp["x_dtype"], seed,
                            outlier_frac=0.01, outlier_mult=20.0)
-    if name == "w4a16_decode":
+    if name in ("w4a16_decode", "w4a16_prefill"):
         return w4a16_inputs(shp["M"], shp["K"], shp["N"], shp["group"], seed)
     if name == "w4afp8_moe":
         return moe_inputs(shp["E"], shp["K"], shp["N"], shp["group"], shp["T"], shp["topk"], seed)

@@ -473,36 +473,56 @@ def test_static_quant_and_gemm(dtype, code):
 
 @pytest.mark.parametrize("N,K,group,zero", [(136, 192, 64, True), (1000, 4096, 128, False), (264, 1536, 512, True)])
 def test_w4a16_dequantize(N, K, group, zero):
+    """Bit-exact against the oracle's bf16 dequantization (one float32
+    evaluation, one rounding to bf16, nearest even)."""
     d = W.w4a16_inputs(4, K, N, group, seed=N + K + group)
     print(f"\n[dequantize] N={N} K={K} g={group} zero={zero}", flush=True)
     z = dev_half(d["zero"], "bf16") if zero else None
     wd = ops.w4a16_dequantize(torch.from_numpy(d["w"]).to(DEV), dev_half(d["scale"], "bf16"), z, group)
     zb = d["zero"] if zero else np.zeros_like(d["zero"])
-    ref = O.dequantize_groupwise(O.unpack_nibble_bytes(d["w"]), O.bf16_bits_to_f32(d["scale"]),
-                                 O.bf16_bits_to_f32(zb), group)
-    got = to_f64(wd)
-    # one fp32 fma (2^-24 relative) then bf16 rounding: half a bf16 step, at
-    # most 2^-8 of the value (8 significant bits)
-    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -20) + 1e-38)
+    ref = O.dequantize_bf16(O.unpack_nibble_bytes(d["w"]), d["scale"], zb, group)
+    assert np.array_equal(wd.view(torch.int16).cpu().numpy().view(np.uint16), ref)
 
 
-@pytest.mark.parametrize("M,N,K,group", [(64, 1000, 4096, 64), (300, 264, 1536, 128)])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 64), (37, 264, 192), (256, 256, 64), (300, 520, 1024), (513, 1000, 640),
+                                   (1024, 2048, 4096), (64, 14336, 4096)])
+def test_w4a16_prefill_gemm(M, N, K):
+    """The bf16 GEMM alone on random bf16 operands (ragged tiles in M and N,
+    K of 1 to 64 steps) against the exact product of the same bf16 values."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    xb = W.to_half_bits(rng.standard_normal((M, K), dtype=np.float32), "bf16")
+    wb = W.to_half_bits((rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.05)), "bf16")
+    print(f"\n[prefill gemm] M={M} N={N} K={K}", flush=True)
+    y = ops.w4a16_prefill_gemm(dev_half(xb, "bf16"), dev_half(wb, "bf16"))
+    ref = O.bf16_bits_to_f32(xb).astype(np.float64) @ O.bf16_bits_to_f32(wb).astype(np.float64).T
+    assert_close(to_f64(y), ref, f"prefill gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,group", [(64, 1000, 4096, 64), (300, 264, 1536, 128), (17, 136, 1024, 512)])
 def test_w4a16_prefill_path(M, N, K, group):
-    """Dequantize once, then the platform's bf16 GEMM (F.linear, hipBLASLt).
-    Bound: each dequantized weight is off by at most 2^-8 of itself (bf16,
-    8 significant bits), the bf16 output by 2^-8 of itself, plus fp32
-    accumulation, so |y - y64| <= 2^-7 * sum_k |x w| + 2^-7 |y64| + 1e-3."""
+    """w4a16_prefill (dequantize to bf16 in the workspace, then the bf16 GEMM)
+    against the oracle's prefill reference: the same bf16 weights, exact
+    products and sums."""
     d = W.w4a16_inputs(M, K, N, group, seed=M + N)
     print(f"\n[prefill] M={M} N={N} K={K} g={group}", flush=True)
-    wd = ops.w4a16_dequantize(torch.from_numpy(d["w"]).to(DEV), dev_half(d["scale"], "bf16"),
-                              dev_half(d["zero"], "bf16"), group)
-    y = torch.nn.functional.linear(dev_half(d["x"], "bf16"), wd)
-    ref = O.w4a16_reference(d["x"], d["w"], d["scale"], d["zero"], group)
-    x = O.bf16_bits_to_f32(d["x"]).astype(np.float64)
-    wabs = np.abs(O.dequantize_groupwise(O.unpack_nibble_bytes(d["w"]), O.bf16_bits_to_f32(d["scale"]),
-                                         O.bf16_bits_to_f32(d["zero"]), group))
-    bound = 2.0 ** -7 * (np.abs(x) @ wabs.T) + 2.0 ** -7 * np.abs(ref) + 1e-3
-    assert np.all(np.abs(to_f64(y) - ref) <= bound)
+    y = ops.w4a16_prefill(dev_half(d["x"], "bf16"), torch.from_numpy(d["w"]).to(DEV), dev_half(d["scale"], "bf16"),
+                          dev_half(d["zero"], "bf16"), group)
+    ref = O.w4a16_prefill_reference(d["x"], d["w"], d["scale"], d["zero"], group)
+    assert_close(to_f64(y), ref, f"prefill {M}x{N}x{K} g{group}")
+
+
+def test_w4a16_prefill_workload():
+    """The prefill workload at full size (M=4096, K=4096, N=14336, group 64) as
+    the benchmark launches it; the oracle on a sample of rows."""
+    d = W.named("w4a16_prefill")
+    print(f"\n[prefill workload] M={d['M']} N={d['N']} K={d['K']} g={d['group']}", flush=True)
+    y = ops.w4a16_prefill(dev_half(d["x"], "bf16"), torch.from_numpy(d["w"]).to(DEV), dev_half(d["scale"], "bf16"),
+                          dev_half(d["zero"], "bf16"), d["group"])
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(11).choice(d["M"], 48, replace=False))
+    ref = O.w4a16_prefill_reference(d["x"][rows], d["w"], d["scale"], d["zero"], d["group"])
+    assert_close(to_f64(y[torch.from_numpy(rows).to(DEV)]), ref, "prefill workload")
+    assert torch.isfinite(y.float()).all()
 
 
 # ------------------------------------------------------------------ asymmetric activations

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
                  "w4_repack_bytes", "w4a8_gemm_partials", "w4a16_tiled_gemm", "w4_linear", "w4_linear_workspace_bytes",
                  "w4_quantize_groupwise", "w4a16_embedding", "w4a8_quantize_act_static", "w4a16_dequantize",
                  "w4a8_quantize_act_asym", "w4a8_weight_offsets", "w4a8_gemm_asym",
-                 "w4_pack_nibbles", "w4_unpack_nibbles", "w4_last_error", "w4_version"):
+                 "w4_pack_nibbles", "w4_unpack_nibbles", "w4a16_prefill_gemm", "w4a16_prefill",
+                 "w4a16_prefill_workspace_bytes", "w4_linear_noalloc", "w4_last_error", "w4_version"):
         assert must in names
 
 
@@ -195,3 +196,19 @@ def test_noalloc_scratch_limit(L):
     assert rc == -5 and "scratch" in _err(L)
     assert L.w4_linear_noalloc(p(256), 1, p(256), p(256), 1, 128, None, p(256), 64, 256, 4096, 0, None) == -4
     assert L.w4_linear_noalloc(None, 1, None, None, 2, 128, None, None, 0, 256, 4096, 0, None) == 0
+
+
+def test_prefill_entry_points_validate(L):
+    p = ctypes.c_void_p
+    n = ctypes.c_size_t()
+    assert L.w4a16_prefill_workspace_bytes(14336, 4096, ctypes.byref(n)) == 0 and n.value == 14336 * 4096 * 2
+    assert L.w4a16_prefill_gemm(p(256), p(256), p(256), 16, 256, 96, None) == -2        # K % 64
+    assert L.w4a16_prefill_gemm(p(256), p(256), p(256), 16, 252, 128, None) == -2       # N % 8
+    assert L.w4a16_prefill_gemm(p(256 + 8), p(256), p(256), 16, 256, 128, None) == -2   # alignment
+    assert L.w4a16_prefill_gemm(None, p(256), p(256), 16, 256, 128, None) == -1
+    assert L.w4a16_prefill_gemm(None, None, None, 0, 256, 128, None) == 0               # empty
+    # dequantize + GEMM: group rule, dtype, workspace size, all before any launch
+    assert L.w4a16_prefill(p(256), p(256), p(256), None, 1, 96, p(256), 16, 256, 384, p(256), 1 << 20, None) == -3
+    assert L.w4a16_prefill(p(256), p(256), p(256), None, 2, 64, p(256), 16, 256, 384, p(256), 1 << 20, None) == -4
+    rc = L.w4a16_prefill(p(256), p(256), p(256), None, 1, 64, p(256), 16, 256, 384, p(256), 100, None)
+    assert rc == -1 and "workspace" in _err(L)
