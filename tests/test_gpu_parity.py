@@ -485,17 +485,21 @@ def test_w4a16_dequantize(N, K, group, zero):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 8, 64), (37, 264, 192), (256, 256, 64), (300, 520, 1024), (513, 1000, 640),
-                                   (1024, 2048, 4096), (64, 14336, 4096)])
+                                   (1024, 2048, 4096), (64, 14336, 4096),
+                                   (4096, 8192, 128), (2100, 8200, 192)])   # these two take 256-column tiles
 def test_w4a16_prefill_gemm(M, N, K):
     """The bf16 GEMM alone on random bf16 operands (ragged tiles in M and N,
-    K of 1 to 64 steps) against the exact product of the same bf16 values."""
+    K of 1 to 64 steps, both tile widths) against the exact product of the
+    same bf16 values (a row sample above 1024 rows)."""
     rng = np.random.default_rng(M * 7 + N + K)
     xb = W.to_half_bits(rng.standard_normal((M, K), dtype=np.float32), "bf16")
     wb = W.to_half_bits((rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.05)), "bf16")
     print(f"\n[prefill gemm] M={M} N={N} K={K}", flush=True)
     y = ops.w4a16_prefill_gemm(dev_half(xb, "bf16"), dev_half(wb, "bf16"))
-    ref = O.bf16_bits_to_f32(xb).astype(np.float64) @ O.bf16_bits_to_f32(wb).astype(np.float64).T
-    assert_close(to_f64(y), ref, f"prefill gemm {M}x{N}x{K}")
+    rows = np.arange(M) if M <= 1024 else np.unique(np.concatenate(
+        [np.random.default_rng(M).choice(M, 64, replace=False), [0, M - 1]]))
+    ref = O.bf16_bits_to_f32(xb[rows]).astype(np.float64) @ O.bf16_bits_to_f32(wb).astype(np.float64).T
+    assert_close(to_f64(y[torch.from_numpy(rows).to(DEV)]), ref, f"prefill gemm {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K,group", [(64, 1000, 4096, 64), (300, 264, 1536, 128), (17, 136, 1024, 512)])
