@@ -62,6 +62,14 @@ __device__ __forceinline__ T wave_max(T v) {
   return v;
 }
 
+// Workgroup barrier without the memory wait that __syncthreads() places
+// before it (s_waitcnt vmcnt(0) lgkmcnt(0), which also drains loads issued
+// for later steps). The caller first waits, with a partial count, for exactly
+// what the other waves need from it (its share of the next stage's LDS DMA,
+// its LDS writes); loads for later steps stay in flight across the barrier.
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
 // Map a linear block id to a tile id so that blocks the hardware sends to
 // the same XCD (round-robin over 8 XCDs) get a contiguous run of tile ids.
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
