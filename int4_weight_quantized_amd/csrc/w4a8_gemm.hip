@@ -446,13 +446,16 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       }
       lstore_b(IC<ST ^ 1>{});
     }
-    if constexpr (MODE == kModeChannel)
+    if constexpr (MODE == kModeChannel) {
       __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): tile tk + 2's B and A may stay in flight
-    else if constexpr (kPingPong)
+      barrier_keep_loads();
+    } else if constexpr (kPingPong) {
       __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): tile tk + 2's A may stay in flight
-    else
+      barrier_keep_loads();
+    } else {
       wait_loads();
-    __syncthreads();
+      __syncthreads();                      // (and the B stores to LDS)
+    }
   };
 
   int tk = kt0;
