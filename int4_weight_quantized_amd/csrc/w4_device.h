@@ -45,10 +45,8 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  // round to nearest even; inputs here are finite
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
