@@ -231,7 +231,13 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     gload_a(min(tk + 2, KT - 1), st == 0 ? 2 : st - 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const v8i bf = unpack_b(j);
+      v8i bf = unpack_b(j);
+      // the unpacked words exist before their registers are reloaded, so the
+      // reload lands in the registers it replaces. (Without this the loads
+      // were hoisted into fresh registers and copied back at the loop end
+      // behind a wait for every load in flight, the A tile two steps ahead
+      // included.)
+      asm volatile("" : "+v"(bf)::"memory");
       gload_b(tn1, j);                       // this block's words of the next step
 #pragma unroll
       for (int i = 0; i < 4; ++i)
