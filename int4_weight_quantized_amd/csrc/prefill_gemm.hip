@@ -21,7 +21,11 @@
 //   so each lane's four results are four consecutive output columns of one
 //   row. A K step is two 32-deep substeps; the fragments of the next substep
 //   (or the next step's first) are read from LDS while the current substep's
-//   64 MFMAs run.
+//   MFMAs run, and so are the DMAs of the tile two steps ahead: one read or
+//   DMA every two to four MFMAs. With one wave per SIMD nothing else feeds
+//   the matrix core, so issuing them in a burst before the MFMAs left it
+//   idle while the wave waited to issue them (405 -> 335 us at M=4096,
+//   K=4096, N=14336).
 // - The output tile goes through LDS in two 128-row halves and leaves as
 //   16-byte row segments (v_cvt_pk_bf16_f32: nearest even).
 // - Tiles are visited in groups of 4 tile-rows, block ids remapped so each XCD
@@ -84,19 +88,23 @@ __global__ __launch_bounds__(kPThreads, 1) void bf16_gemm_nt_kernel(const uint16
   const uint32_t lchunk_off = 16u * (uint32_t)(lchunk ^ lrow);
   const uint32_t xoff = (uint32_t)(64 * wave + lrow) * rowb + lchunk_off;
   const uint32_t woff = (uint32_t)(BN / 4 * wave + lrow) * rowb + lchunk_off;
-  auto gload = [&](int tk, int st) {
+  // DMA instruction o of a K step: o < 8 a row group of x, else one of w
+  auto gload_one = [&](int tk, int st, int o) {
     const uint32_t ks = (uint32_t)tk * kPRow;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
+    if (o < 8)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (__attribute__((address_space(3))) void*)(lds + st * kPStage + (64 * wave_u + 8 * i) * kPRow), 16,
-          xoff + ks + (uint32_t)(8 * i) * rowb, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < BN / 32; ++i)
+          xr, (__attribute__((address_space(3))) void*)(lds + st * kPStage + (64 * wave_u + 8 * o) * kPRow), 16,
+          xoff + ks + (uint32_t)(8 * o) * rowb, 0, 0, 0);
+    else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wr,
-          (__attribute__((address_space(3))) void*)(lds + st * kPStage + kPStageA + (BN / 4 * wave_u + 8 * i) * kPRow),
-          16, woff + ks + (uint32_t)(8 * i) * rowb, 0, 0, 0);
+          (__attribute__((address_space(3))) void*)(lds + st * kPStage + kPStageA +
+                                                    (BN / 4 * wave_u + 8 * (o - 8)) * kPRow),
+          16, woff + ks + (uint32_t)(8 * (o - 8)) * rowb, 0, 0, 0);
+  };
+  auto gload = [&](int tk, int st) {
+#pragma unroll
+    for (int o = 0; o < 8 + BN / 32; ++o) gload_one(tk, st, o);
   };
   constexpr int kLoads = 8 + BN / 32;           // DMA instructions per wave and K step
 
@@ -115,18 +123,18 @@ __global__ __launch_bounds__(kPThreads, 1) void bf16_gemm_nt_kernel(const uint16
 #pragma unroll
     for (int j = 0; j < NJ; ++j) wf[buf][j] = *reinterpret_cast<const v8bf*>(base + wo + 16 * kPRow * j);
   };
+  // fragment read r of a substep: r < 8 an x row block, else a w column block
+  auto read_one = [&](int st, int s, int buf, int r) {
+    const uint8_t* base = lds + st * kPStage + fo[s];
+    if (r < 8) xf[buf][r] = *reinterpret_cast<const v8bf*>(base + xo + 16 * kPRow * r);
+    else wf[buf][r - 8] = *reinterpret_cast<const v8bf*>(base + wo + 16 * kPRow * (r - 8));
+  };
 
   v4f acc[8][NJ];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto mfmas = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) mfma_acc(acc[i][j], wf[buf][j], xf[buf][i]);
-  };
 
   // ---- prologue: tiles 0 and 1 into the two stages, tile 0's first fragments
   gload(0, 0);
@@ -141,19 +149,32 @@ __global__ __launch_bounds__(kPThreads, 1) void bf16_gemm_nt_kernel(const uint16
   // tk + 2 starts streaming into stage st, and substep 1 runs while the next
   // step's first fragments are read. A tile has about a whole K step of MFMAs
   // to arrive.
+  constexpr int kNM = 8 * NJ, kNR = 8 + NJ;   // MFMAs and fragment reads per substep
   auto kstep = [&](int tk, int st) {
-    read_frags(st, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
+    // substep 0's MFMAs with substep 1's fragment reads spread among them
+#pragma unroll
+    for (int r = 0; r < kNR; ++r) {
+      read_one(st, 1, 1, r);
+#pragma unroll
+      for (int q = (r * kNM) / kNR; q < ((r + 1) * kNM) / kNR; ++q)
+        mfma_acc(acc[q / NJ][q % NJ], wf[0][q % NJ], xf[0][q / NJ]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    gload(min(tk + 2, KT - 1), st);
-    read_frags(st ^ 1, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
+    // substep 1's MFMAs with tile tk + 2's DMAs and the next step's first
+    // fragment reads spread among them
+    const int tn2 = min(tk + 2, KT - 1);
+#pragma unroll
+    for (int o = 0; o < 2 * kLoads; ++o) {
+      if (o % 2 == 0) gload_one(tn2, st, o / 2);
+      else read_one(st ^ 1, 0, 0, o / 2);
+#pragma unroll
+      for (int q = (o * kNM) / (2 * kLoads); q < ((o + 1) * kNM) / (2 * kLoads); ++q)
+        mfma_acc(acc[q / NJ][q % NJ], wf[1][q % NJ], xf[1][q / NJ]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   int tk = 0;
   for (; tk + 1 < KT; tk += 2) {
