@@ -29,6 +29,12 @@
 //   holding K 32q .. 32q+31 of column c, whose low nibbles are K 32q..+15 and
 //   high nibbles K 32q+16..+31 -- exactly the 32 fp8 bytes the MFMA wants
 //   from that lane, matching the A fragment (logical chunks 2q, 2q+1).
+// - With group 128 (a whole group per K step) the MFMAs are asm statements,
+//   so that they keep their order, and the vector work of the step is placed
+//   between them: block j's four MFMAs carry block j + 1's unpack and reload
+//   and block j - 1's epilogue (left to the compiler, the unpack all came
+//   first and the epilogue all last). The stage index and the K offset of the
+//   A DMA are scalar. Other group sizes use the builtin MFMA.
 // - One K step per loop iteration, the stage index in a register. A step
 //   first reads all of its A fragments and C starts (before it issues its
 //   own LDS DMA, so those reads wait for nothing newer than the previous
@@ -110,13 +116,15 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     const int tok = s_tok[32 * wave + 8 * i + lrow];
     a_voff[i] = (tok >= 0) ? (uint32_t)tok * (uint32_t)K + a_chunk : 0x80000000u;
   }
+  // the K offset goes in the scalar operand: a row without a token stays
+  // past the buffer through its VGPR offset alone
   auto gload_a = [&](int tk, int st) {
     const uint32_t ks = (uint32_t)tk * kEK;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           arsrc, (__attribute__((address_space(3))) void*)(lds + st * kEStageA + (32 * wave_u + 8 * i) * kEK), 16,
-          a_voff[i] + ks, 0, 0, 0);
+          a_voff[i], ks, 0, 0);
   };
 
   // ---- B straight into registers: lane (column l%16 of 16-column block j,
@@ -181,6 +189,30 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) facc[i][j][r] = fmaf(acc[i][j][r], sc, facc[i][j][r]);
   };
+  // rows [R0, R0 + 2) of block j's group epilogue
+  auto epilogue_rows = [&](int j, int R0, const eh2 (&raw)[2]) {
+    const float sc = (float)raw[j >> 1][j & 1];
+#pragma unroll
+    for (int i = R0; i < R0 + 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) facc[i][j][r] = fmaf(acc[i][j][r], sc, facc[i][j][r]);
+  };
+  // d = a * b + c (fp8 x fp8, block scales 2^0 and 2^9), written as asm so
+  // that it keeps its place among the unpack and epilogue work around it.
+  // Its result is read by vector code only four or more MFMAs later.
+  const uint32_t scale_a = 127u, scale_b = 136u;
+  // pins: vector work placed between two of these stays between the MFMAs
+  // around them (asm statements keep their order)
+  auto pin_facc = [&](int j, int R0) {
+    asm volatile("" : "+v"(facc[R0][j][0]), "+v"(facc[R0][j][1]), "+v"(facc[R0][j][2]), "+v"(facc[R0][j][3]),
+                 "+v"(facc[R0 + 1][j][0]), "+v"(facc[R0 + 1][j][1]), "+v"(facc[R0 + 1][j][2]),
+                 "+v"(facc[R0 + 1][j][3]));
+  };
+  auto mfma_fresh = [&](v4f& d, const v8i& a, const v8i& b, const v4f& c) {
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %3, %4, %5 op_sel_hi:[0,0,0]"
+                 : "=&v"(d)
+                 : "v"(a), "v"(b), "v"(c), "v"(scale_a), "v"(scale_b));
+  };
   // ---- A fragments: lane row (lane & 15), logical chunks 2g and 2g + 1 at
   // physical chunks g ^ (row & 7) and (4 + g) ^ (row & 7)
   const int fl = lane & 7, g4 = lane >> 4;
@@ -214,7 +246,8 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   // tk + 1's A has landed and its sums are stored (the 13 newest loads may
   // stay in flight across the barrier).
   bool last_prev = false;                  // did the previous step end a group?
-  auto kstep = [&](int tk, int st) {
+  auto kstep = [&](int tk, int st_) {
+    const int st = __builtin_amdgcn_readfirstlane(st_);
     const bool fresh = (tk % GT) == 0, last = (tk % GT) == GT - 1;
     const int tn1 = min(tk + 1, KT - 1);
     // this step's fragments first: read before this step's DMA is issued,
@@ -229,14 +262,46 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     fetch_scales(tn1, sc_next);
     const float gs_new = gload_gs(min(tk + 2, KT - 1));
     gload_a(min(tk + 2, KT - 1), st == 0 ? 2 : st - 1);
+    if constexpr (GT == 1) {
+      // every step is one whole group: block j's four MFMAs carry block
+      // j + 1's unpack and reload and block j - 1's epilogue between them
+      v8i bf = unpack_b(0);
+      asm volatile("" : "+v"(bf)::"memory");
+      gload_b(tn1, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v8i bn = bf;
+        const bool epi = j > 0 || last_prev;
+        const int je = j == 0 ? 3 : j - 1;
+        mfma_fresh(acc[0][j], af[0], bf, ci[0]);
+        if (j < 3) {
+          asm volatile("" : "+v"(pb[j + 1]));
+          bn = unpack_b(j + 1);
+        }
+        mfma_fresh(acc[1][j], af[1], bf, ci[1]);
+        if (j < 3) {
+          asm volatile("" : "+v"(bn)::"memory");
+          gload_b(tn1, j + 1);
+        }
+        mfma_fresh(acc[2][j], af[2], bf, ci[2]);
+        if (epi) {
+          pin_facc(je, 0);
+          epilogue_rows(je, 0, j == 0 ? sc_prev : sc_cur);
+          pin_facc(je, 0);
+        }
+        mfma_fresh(acc[3][j], af[3], bf, ci[3]);
+        if (epi) {
+          pin_facc(je, 2);
+          epilogue_rows(je, 2, j == 0 ? sc_prev : sc_cur);
+          pin_facc(je, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf = bn;
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v8i bf = unpack_b(j);
-      // the unpacked words exist before their registers are reloaded, so the
-      // reload lands in the registers it replaces. (Without this the loads
-      // were hoisted into fresh registers and copied back at the loop end
-      // behind a wait for every load in flight, the A tile two steps ahead
-      // included.)
       asm volatile("" : "+v"(bf)::"memory");
       gload_b(tn1, j);                       // this block's words of the next step
 #pragma unroll
@@ -248,6 +313,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       } else if (last) {
         epilogue(j - 1, sc_cur);
       }
+    }
     }
     last_prev = last;
 #pragma unroll
@@ -266,6 +332,8 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   for (int tk = 0, st = 0; tk < KT; ++tk, st = (st == 2 ? 0 : st + 1)) kstep(tk, st);
   // the clamped last loads may still be streaming into LDS
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+  // the last MFMAs' results: wait states before vector code reads them
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   if (last_prev) epilogue(3, sc_prev);
 
   // ---- output: row scale, bf16, staged through LDS and written as 16-byte
