@@ -469,6 +469,36 @@ def test_static_quant_and_gemm(dtype, code):
         assert np.all(np.abs(gs.cpu().numpy() - dec.sum(-1)) <= 1e-6 * np.abs(dec).sum(-1) + 1e-30)
 
 
+def test_fp8_static_quotients_near_midpoints():
+    """The FP8 conversion at every decision boundary: E4M3 midpoints share 16
+    significands across binades (the normal ones (2k+1)/16 above 1, the
+    subnormal ones k/8), so a row of signed powers of two divided by a
+    calibrated scale s = 1/t, with t one of those significands moved by up to
+    four float32 steps, puts quotients within a few steps of every midpoint,
+    below the smallest subnormal and past 448. Each code is compared with the
+    oracle's encoding of the float32 quotient."""
+    sig = [1.0 + (2 * k + 1) / 16.0 for k in range(8)] + [k / 8.0 for k in range(8, 16)]
+    e = np.arange(-20, 21)
+    row = np.concatenate([np.exp2(e), -np.exp2(e)]).astype(np.float32)
+    row = np.concatenate([row, np.zeros((-row.size) % 8, np.float32)])
+    xb = O.f32_to_bf16_bits(row[None, :])
+    assert np.array_equal(O.bf16_bits_to_f32(xb)[0], row)                     # powers of two: exact in bf16
+    x = dev_half(xb, "bf16")
+    x32 = O.bf16_bits_to_f32(xb)
+    n_checked = 0
+    for p in sig:
+        for k in range(-4, 5):
+            t = np.float32(p) + np.float32(k) * np.spacing(np.float32(p))
+            s_static = np.float32(np.float32(1.0) / t)
+            sd = torch.tensor([s_static], dtype=torch.float32, device=DEV)
+            codes, _, _ = ops.w4a8_quantize_act_static(x, sd, "fp8")
+            ref = O.e4m3_encode((x32 / s_static).astype(np.float32))
+            got = codes.cpu().numpy()
+            assert np.array_equal(got, ref), (p, k, float(s_static), int(np.sum(got != ref)))
+            n_checked += row.size
+    print(f"\n[fp8 static midpoints] {n_checked} quotients", flush=True)
+
+
 # ------------------------------------------------------------------ prefill: dequantize once, ordinary GEMM
 
 @pytest.mark.parametrize("N,K,group,zero", [(136, 192, 64, True), (1000, 4096, 128, False), (264, 1536, 512, True)])
