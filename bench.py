@@ -25,7 +25,8 @@ Measured in the same run and reported beside it:
   cpu_baseline  the CPU oracle timed on a bounded row sample of the step
 
 Before the first timed region the W4A8 step runs untimed for --settle-s
-seconds (0.5): the clocks take a fraction of a second of load to settle.
+seconds (0.5), and each later GEMM section for half that: the clocks take a
+fraction of a second of load to settle.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only w4a8|decode|moe]
        python bench.py --calib-copy
@@ -122,6 +123,16 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
         return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(dev)
 
+    def settle(fns, seconds):
+        """Run the callables untimed for about `seconds`: the engine clock
+        needs a fraction of a second of load to reach its steady state."""
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                for f in fns:
+                    f()
+            torch.cuda.synchronize()
+
     def timed(fns, steps, warmup, per_call=True):
         """Run the list of launch callables per step; return mean ms per callable
         (HIP events on the launch stream; None without per_call), the mean
@@ -182,12 +193,7 @@ def main():
     fq = lambda: ops.quantize_act_into(x, codes, s_a)
     fg = lambda: ops.w4a8_gemm(codes, s_a, wt, sc, g, N, out=y)
     # untimed steps until the clocks settle, then the W warmup steps and the K timed ones
-    t_end = time.perf_counter() + args.settle_s
-    while time.perf_counter() < t_end:
-        for _ in range(8):
-            fq()
-            fg()
-        torch.cuda.synchronize()
+    settle([fq, fg], args.settle_s)
     (t_q, t_g), t_step, _ = timed([fq, fg], args.steps, args.warmup)
     ops_gemm = 2.0 * M * N * K
     tops = ops_gemm / (t_step * 1e-3) / 1e12
@@ -230,6 +236,7 @@ def main():
         woff = ops.w4a8_weight_offsets(wt, sc, g, K, N)
         fqa = lambda: ops.w4a8_quantize_act_asym_into(x, codes, s_a, z_a)
         fga = lambda: ops.w4a8_gemm_asym(codes, s_a, z_a, wt, sc, g, woff, N, out=y)
+        settle([fqa, fga], args.settle_s / 2)
         (t_qa, t_ga), t_sa, _ = timed([fqa, fga], max(4, args.steps // 2), max(2, args.warmup // 2))
         asym = {"workload": f"w4a8_up_proj asymmetric per-token activations M={M} K={K} N={N} group={g}",
                 "quant_ms": t_qa, "gemm_ms": t_ga, "step_ms": t_sa,
@@ -248,6 +255,7 @@ def main():
         y_d = torch.empty((Md, Nd), dtype=torch.float16, device=dev)
         fqd = lambda: ops.quantize_act_into(xd, codes_d, s_d)
         fgd = lambda: ops.w4a8_gemm(codes_d, s_d, wtd, scd, gd, Nd, out=y_d)
+        settle([fqd, fgd], args.settle_s / 2)
         (t_qd, t_gd), t_sd, _ = timed([fqd, fgd], max(4, args.steps // 2), max(2, args.warmup // 2))
         ops_d = 2.0 * Md * Nd * Kd
         down = {"workload": f"w4a8_down_proj M={Md} K={Kd} N={Nd} group={gd} f16 (1% outlier channels x20)",
@@ -316,8 +324,10 @@ def main():
         f_dq = lambda: ops.w4a16_dequantize(wb, sp, zp, gp, out=wdq)
         f_mm = lambda: ops.w4a16_prefill_gemm(xp, wdq, out=yp)          # the library's bf16 GEMM
         f_blas = lambda: torch.matmul(xp, wdq.t(), out=yp)              # baseline: the platform GEMM (hipBLASLt)
-        (t_dq, t_mm), t_pf, _ = timed([f_dq, f_mm], max(4, args.steps // 5), max(2, args.warmup // 2))
-        (t_blas,), _, _ = timed([f_blas], max(4, args.steps // 5), max(2, args.warmup // 2))
+        settle([f_dq, f_mm], args.settle_s / 2)
+        (t_dq, t_mm), t_pf, _ = timed([f_dq, f_mm], max(4, args.steps // 2), max(2, args.warmup // 2))
+        settle([f_blas], args.settle_s / 2)
+        (t_blas,), _, _ = timed([f_blas], max(4, args.steps // 2), max(2, args.warmup // 2))
         dq_bytes = Np * Kp // 2 + 2 * 2 * Np * (Kp // gp) + 2 * Np * Kp
         fl = 2.0 * Mp * Np * Kp
         prefill = {"workload": f"w4a16 prefill M={Mp} K={Kp} N={Np} group={gp} bf16 (dequantize + bf16 GEMM)",
@@ -346,6 +356,7 @@ def main():
         ym = torch.empty((R, Nm), dtype=torch.bfloat16, device=dev)
         fq8 = lambda: ops.quantize_act_into(xm, a8, sm, gs, gm, fp8=True)
         fgg = lambda: ops.w4a8_grouped_gemm(a8, sm, gs, rt, off, wm, scm, gm, Nm, out=ym)
+        settle([fq8, fgg], args.settle_s / 2)
         (t_q8, t_gg), t_moe, _ = timed([fq8, fgg], max(2, args.steps // 4), max(1, args.warmup // 2))
         flops = 2.0 * R * Nm * Km
         moe = {"workload": f"w4afp8_moe E={Em} K={Km} N={Nm} group={gm} T={Tm} top{dm['topk']} R={R}",
@@ -399,6 +410,7 @@ def main():
         try:
             a8 = torch.randint(-127, 128, (8192, 8192), dtype=torch.int8, device=dev)
             b8 = torch.randint(-127, 128, (8192, 8192), dtype=torch.int8, device=dev)
+            settle([lambda: torch._int_mm(a8, b8)], args.settle_s / 2)
             (t_i8,), _, _ = timed([lambda: torch._int_mm(a8, b8)], 10, 3)
             mp["int8_gemm_tops"] = 2.0 * 8192 ** 3 / (t_i8 * 1e-3) / 1e12
             del a8, b8
@@ -406,6 +418,7 @@ def main():
             mp["int8_gemm_error"] = type(ex).__name__
         ab = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
         bb = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+        settle([lambda: torch.matmul(ab, bb)], args.settle_s / 2)
         (t_bf,), _, _ = timed([lambda: torch.matmul(ab, bb)], 10, 3)
         mp["bf16_gemm_tflops"] = 2.0 * 8192 ** 3 / (t_bf * 1e-3) / 1e12
         del ab, bb
