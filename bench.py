@@ -28,7 +28,7 @@ Before the first timed region the W4A8 step runs untimed for --settle-s
 seconds (0.5), and each later GEMM section for half that: the clocks take a
 fraction of a second of load to settle.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only w4a8|decode|moe]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only w4a8|down|decode|prefill|moe|vocab]
        python bench.py --calib-copy
 """
 from __future__ import annotations
@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--only", choices=["all", "w4a8", "down", "decode", "moe", "vocab", "shards"], default="all",
+    p.add_argument("--only", choices=["all", "w4a8", "down", "decode", "prefill", "moe", "vocab", "shards"], default="all",
                    help="which extra measurements to add to the W4A8 step (shards: only when asked for)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     p.add_argument("--settle-s", type=float, default=0.5,
@@ -313,7 +313,7 @@ def main():
 
     # ------------------------------------------------------------ W4A16 prefill: dequantize once + bf16 GEMM
     prefill = {}
-    if args.only in ("all", "decode"):
+    if args.only in ("all", "decode", "prefill"):
         dd = W.named("w4a16_decode", M=1)
         Kp, Np, gp, Mp = dd["K"], dd["N"], dd["group"], 4096
         wb = torch.from_numpy(dd["w"]).to(dev)
