@@ -136,7 +136,9 @@ def main():
     def timed(fns, steps, warmup, per_call=True):
         """Run the list of launch callables per step; return mean ms per callable
         (HIP events on the launch stream; None without per_call), the mean
-        step time and the wall time.
+        step time and the wall time. With per_call the steps run twice: once
+        with an event between callables (the per-callable times) and once
+        without (the step time, free of the events' own cost).
         The timed launches must run back to back, without host launch gaps.
         When a step's GPU time is well above its host enqueue time (the GEMMs),
         the timed steps are simply enqueued behind a second round of warmup
@@ -162,17 +164,22 @@ def main():
                 for f in fns:
                     f()
         else:
-            # shader-clock cycles at up to 2.4 GHz; twice the host enqueue time, at most ~0.1 s
-            torch.cuda._sleep(int(min(0.1, 2.0 * host_per_step * steps + 1e-3) * 2.4e9))
+            # shader-clock cycles at up to 2.4 GHz; twice the host enqueue time of
+            # both timed regions, at most ~0.2 s
+            rounds = 2 if per_call else 1
+            torch.cuda._sleep(int(min(0.2, 2.0 * host_per_step * steps * rounds + 1e-3) * 2.4e9))
         t0 = time.perf_counter()
+        if per_call:
+            # the per-callable region, enqueued right ahead of the step region
+            for s in range(steps):
+                ev[s][0].record(stream)
+                for i, f in enumerate(fns):
+                    f()
+                    ev[s][i + 1].record(stream)
         start.record(stream)
         for s in range(steps):
-            if per_call:
-                ev[s][0].record(stream)
-            for i, f in enumerate(fns):
+            for f in fns:
                 f()
-                if per_call:
-                    ev[s][i + 1].record(stream)
         end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
