@@ -60,6 +60,32 @@ def test_int8_bruteforce_all_bf16_patterns():
         assert np.array_equal(codes[0].astype(np.int64), ref)
 
 
+def test_int8_quotients_near_half_steps():
+    """Rows at non-power-of-two absmax whose float32 values put fl32(x/scale)
+    within a few float32 steps of every half-integer k + 1/2: the code is
+    decided by the correctly rounded float32 quotient (exact rationals here),
+    which a reciprocal multiply or a float64 scale gets wrong at some of
+    them."""
+    for amax in (3.0, 7.25, 0.3, 1e-3, 5.5, 123.4, 0.07):
+        amax32 = np.float32(amax)
+        s_ref = _f32(float(amax32) / 127.0)
+        xs = []
+        for k in range(127):
+            c = np.float32(float(Fraction(2 * k + 1, 2) * Fraction(s_ref)))
+            for _ in range(3):
+                c = np.nextafter(c, np.float32(0))
+            for _ in range(7):
+                if abs(c) <= amax32:
+                    xs += [c, -c]
+                c = np.nextafter(c, np.float32(1e30))
+        x = np.array([amax32] + xs, dtype=np.float32)[None, :]
+        codes, s = O.quantize_act_int8(x)
+        assert float(s[0]) == s_ref
+        ref = [max(-127, min(127, _rne_int(Fraction(_f32(float(Fraction(float(t)) / Fraction(s_ref)))))))
+               for t in x[0]]
+        assert codes[0].astype(np.int64).tolist() == ref, amax
+
+
 def test_int8_invariants_random_rows():
     rng = np.random.default_rng(7)
     x = (rng.standard_normal((64, 300)) * rng.uniform(1e-3, 1e3, (64, 1))).astype(np.float32)
