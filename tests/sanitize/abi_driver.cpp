@@ -62,6 +62,59 @@ int main() {
   expect(w4_quantize_groupwise(p, W4_I8, 4, 256, 64, (uint8_t*)p, p, p, W4_F32, nullptr), W4_ERR_DTYPE, "qg dt");
   expect(w4a16_embedding(nullptr, 4, p, p, 64, 100, 256, p, nullptr), W4_ERR_ALIGN, "emb V");
   expect(w4a16_embedding(nullptr, 4, p, p, 64, 128, 256, p, nullptr), W4_ERR_INVALID, "emb null");
+  expect(w4_linear_noalloc(p, W4_BF16, p, p, W4_F16, 128, nullptr, p, 32768, 14336, 4096, 0, nullptr),
+         W4_ERR_UNSUPPORTED, "na scratch");
+  expect(w4_linear_noalloc(p, W4_BF16, p, p, W4_F16, -1, nullptr, p, 64, 256, 132160, 0, nullptr), W4_ERR_UNSUPPORTED,
+         "na group");
+  expect(w4_linear_noalloc(p, W4_BF16, p, p, W4_F16, 128, nullptr, odd, 4, 256, 4096, 0, nullptr), W4_ERR_ALIGN,
+         "na out");
+  expect(w4_linear_noalloc(nullptr, W4_BF16, nullptr, nullptr, W4_F16, 128, nullptr, nullptr, 0, 256, 4096, 0, nullptr),
+         W4_OK, "na empty");
+  // asymmetric int8 path
+  expect(w4a8_quantize_act_asym(p, W4_BF16, 4, 252, 256, (int8_t*)p, (float*)p, (float*)p, nullptr), W4_ERR_ALIGN, "qa K");
+  expect(w4a8_quantize_act_asym(p, W4_F32, 4, 256, 256, (int8_t*)p, (float*)p, (float*)p, nullptr), W4_ERR_DTYPE, "qa dt");
+  expect(w4a8_quantize_act_asym(p, W4_BF16, 4, 256, 256, (int8_t*)odd, (float*)p, (float*)p, nullptr), W4_ERR_ALIGN,
+         "qa codes");
+  expect(w4a8_quantize_act_asym(p, W4_BF16, 4, 256, 256, (int8_t*)p, (float*)p, nullptr, nullptr), W4_ERR_INVALID,
+         "qa null");
+  expect(w4a8_quantize_act_asym(nullptr, W4_BF16, 0, 256, 256, nullptr, nullptr, nullptr, nullptr), W4_OK, "qa empty");
+  expect(w4a8_weight_offsets(p, p, W4_BF16, 128, 256, 256, (float*)p, nullptr), W4_ERR_DTYPE, "wo dt");
+  expect(w4a8_weight_offsets(p, p, W4_F16, 96, 288, 256, (float*)p, nullptr), W4_ERR_GROUP, "wo group");
+  expect(w4a8_weight_offsets(p, p, W4_F16, 128, 256, 256, nullptr, nullptr), W4_ERR_INVALID, "wo null");
+  expect(w4a8_weight_offsets(nullptr, nullptr, W4_F16, 128, 256, 0, nullptr, nullptr), W4_OK, "wo empty");
+  expect(w4a8_gemm_asym((const int8_t*)p, (const float*)p, (const float*)p, p, p, W4_F32, 128, (const float*)p, nullptr,
+                        p, W4_BF16, 4, 256, 256, nullptr), W4_ERR_DTYPE, "ga sdt");
+  expect(w4a8_gemm_asym((const int8_t*)p, (const float*)p, (const float*)p, p, p, W4_F16, -1, (const float*)p, nullptr,
+                        p, W4_BF16, 4, 256, 131136, nullptr), W4_ERR_UNSUPPORTED, "ga group");
+  expect(w4a8_gemm_asym((const int8_t*)p, (const float*)p, nullptr, p, p, W4_F16, 128, (const float*)p, nullptr, p,
+                        W4_BF16, 4, 256, 256, nullptr), W4_ERR_INVALID, "ga null");
+  expect(w4a8_gemm_asym((const int8_t*)p, (const float*)p, (const float*)p, p, p, W4_F16, 128, (const float*)p, nullptr,
+                        odd, W4_F16, 4, 256, 256, nullptr), W4_ERR_ALIGN, "ga out");
+  // bf16 weight-only: dequantization and prefill
+  expect(w4a16_dequantize((const uint8_t*)p, p, p, W4_F16, 128, 256, 256, p, nullptr), W4_ERR_DTYPE, "dq dt");
+  expect(w4a16_dequantize((const uint8_t*)p, p, p, W4_BF16, 96, 288, 256, p, nullptr), W4_ERR_GROUP, "dq group");
+  expect(w4a16_dequantize((const uint8_t*)odd, p, p, W4_BF16, 128, 256, 256, p, nullptr), W4_ERR_ALIGN, "dq w");
+  expect(w4a16_dequantize(nullptr, nullptr, nullptr, W4_BF16, 128, 256, 0, nullptr, nullptr), W4_OK, "dq empty");
+  expect(w4a16_prefill_gemm(p, p, p, 16, 256, 96, nullptr), W4_ERR_ALIGN, "pg K");
+  expect(w4a16_prefill_gemm(p, p, p, -1, 256, 256, nullptr), W4_ERR_INVALID, "pg M");
+  expect(w4a16_prefill_gemm(p, p, odd, 16, 256, 256, nullptr), W4_ERR_ALIGN, "pg out");
+  expect(w4a16_prefill_gemm(nullptr, nullptr, nullptr, 0, 256, 256, nullptr), W4_OK, "pg empty");
+  expect(w4a16_prefill_workspace_bytes(14336, 4096, &n), W4_OK, "pw");
+  expect(n == (size_t)14336 * 4096 * 2, 1, "pw size");
+  expect(w4a16_prefill_workspace_bytes(256, 0, &n), W4_ERR_INVALID, "pw K");
+  expect(w4a16_prefill_workspace_bytes(256, 256, nullptr), W4_ERR_INVALID, "pw null");
+  expect(w4a16_prefill(p, (const uint8_t*)p, p, p, W4_BF16, 128, p, 16, 256, 4096, p, 4096, nullptr), W4_ERR_INVALID,
+         "pf ws");
+  expect(w4a16_prefill(p, (const uint8_t*)p, p, p, W4_BF16, 128, p, 16, 256, 4096, odd, (size_t)1 << 21, nullptr),
+         W4_ERR_ALIGN, "pf ws align");
+  expect(w4a16_prefill(p, (const uint8_t*)p, p, p, W4_F16, 64, p, 16, 256, 4096, p, (size_t)1 << 22, nullptr),
+         W4_ERR_DTYPE, "pf dt");
+  // nibble packing
+  expect(w4_pack_nibbles((const uint8_t*)p, 4, 255, (uint8_t*)p, nullptr), W4_ERR_ALIGN, "pk K");
+  expect(w4_pack_nibbles((const uint8_t*)p, -1, 256, (uint8_t*)p, nullptr), W4_ERR_INVALID, "pk N");
+  expect(w4_unpack_nibbles((const uint8_t*)odd, 4, 256, (uint8_t*)p, nullptr), W4_ERR_ALIGN, "upk align");
+  expect(w4_unpack_nibbles(nullptr, 0, 256, nullptr, nullptr), W4_OK, "upk empty");
+  expect(w4_unpack_nibbles((const uint8_t*)p, 4, 256, nullptr, nullptr), W4_ERR_INVALID, "upk null");
   // the longest message paths: every argument named, sizes at their widest
   expect(w4a8_gemm((const int8_t*)p, (const float*)p, p, p, W4_F16, 128, nullptr, p, W4_BF16, 4,
                    (int64_t)1 << 62 | 4, ((int64_t)1 << 62) | 12, nullptr), W4_ERR_UNSUPPORTED, "g huge");

@@ -39,3 +39,15 @@ def test_abi_validation_under_asan_ubsan():
         out = run.stdout + run.stderr
         assert "AddressSanitizer" not in out and "runtime error" not in out, out
         assert run.returncode == 0, out
+
+
+def test_driver_calls_every_declared_entry_point():
+    """The sanitizer driver exercises the validation of every function the
+    header declares, so a new entry point cannot skip the sanitizer run."""
+    import re
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from test_host_abi import _declared_functions
+    drv = open(os.path.join(ROOT, "tests", "sanitize", "abi_driver.cpp")).read()
+    missing = [f for f in _declared_functions() if not re.search(r"\b%s\s*\(" % f, drv)]
+    assert not missing, missing
