@@ -72,7 +72,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 // the kernel ends after the K loop; loads, unpack, LDS layout, MFMAs and
 // their schedule are the ones the epilogue-fused instantiation runs.
 template <int MODE, bool OUT_BF16, int GC, bool PART>
-__global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
+__global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
@@ -226,6 +226,20 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       raw[j >> 1][j & 1] = __builtin_bit_cast(
           _Float16, __builtin_amdgcn_raw_buffer_load_b16(srsrc, s_voff[j], (uint32_t)g * (uint32_t)N * 2u, 0));
   };
+  // the next group's scales, loaded as four halves and paired up only once
+  // the step's closing wait has seen them land: left to itself the compiler
+  // may pair them mid-step, which waits there for every load issued before
+  // them in the same step (the next step's B words included)
+  auto fetch_scales_split = [&](int g, uint32_t (&raw)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      raw[j] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, s_voff[j], (uint32_t)g * (uint32_t)N * 2u, 0);
+  };
+  auto pair_scales = [&](uint32_t (&raw)[4], h2 (&out)[2]) {
+    asm volatile("" : "+v"(raw[0]), "+v"(raw[1]), "+v"(raw[2]), "+v"(raw[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j >> 1][j & 1] = __builtin_bit_cast(_Float16, (uint16_t)raw[j]);
+  };
 
   // group epilogue for sub-tile rows [I0, I1)
   auto epilogue = [&](auto I0c, auto I1c, const h2 (&raw)[2], int g) {
@@ -345,6 +359,15 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     // q), substep 1 the high ones (K 32 q + 16..31); the A fragments follow.
     v4i b0[4], b1[4];
     if constexpr (kPingPong) {
+      if constexpr (MODE == kModeChannel) {
+        // pin this step's unpack after the previous step's barrier: the
+        // compiler otherwise hoists it two steps up, next to the load of
+        // these words, and waits there for that load to land
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (PB == 0) asm volatile("" : "+v"(pb[j])); else asm volatile("" : "+v"(pb2[j]));
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -354,7 +377,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
           b1[j][e] = (int)(w & 0xF0F0F0F0u);
         }
     }
-    h2 scr_next[2];
+    uint32_t scr_next[4];
     if constexpr (MODE == kModeChannel) {
       // B of tile tk + 2 into the registers just unpacked, then its A: the
       // step ends waiting for everything but these eight loads
@@ -363,7 +386,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     } else if constexpr (kPingPong) {
       // loads in this order, A of tile tk + 2 last, so that the step can end
       // waiting for everything but that: vmcnt(4)
-      if constexpr (kStepScales) fetch_scales(min(tk + 1, kt1 - 1), scr_next);
+      if constexpr (kStepScales) fetch_scales_split(min(tk + 1, kt1 - 1), scr_next);
       gload_bd(min(tk + 1, kt1 - 1), IC<0>{});
       gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
     } else {
@@ -422,10 +445,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       epilogue(IC<1>{}, IC<2>{}, scr_cur, tk);
       interleave8();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        scr_prev[j] = scr_cur[j];
-        scr_cur[j] = scr_next[j];
-      }
+      for (int j = 0; j < 2; ++j) scr_prev[j] = scr_cur[j];
     } else {
       // scales of the groups ending in this step (at most two)
       h2 s0[2], s1[2];
@@ -452,6 +472,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     } else if constexpr (kPingPong) {
       __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): tile tk + 2's A may stay in flight
       barrier_keep_loads();
+      if constexpr (kStepScales) pair_scales(scr_next, scr_cur);
     } else {
       wait_loads();
       __syncthreads();                      // (and the B stores to LDS)
