@@ -40,7 +40,7 @@
 //   the other half's finished group goes through its epilogue (int32 ->
 //   fp32, FMA with the group's fp16 scale), so the vector ALU work overlaps
 //   the matrix core. Other group sizes apply the epilogue after each group.
-// - Tiles are visited in groups of 8 tile-rows, and block ids are remapped
+// - Tiles are visited in groups of 8 tile-rows (4 for per-channel weights), and block ids are remapped
 //   so each XCD (own L2) works on a contiguous range of tiles.
 #include <type_traits>
 
@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel
     kt0 = min(split * ks, KT);
     kt1 = min(kt0 + ks, KT);
   }
-  constexpr int GM = 8;
+  // tile-rows per raster group (per-channel: 4 measured ~2% faster than 8)
+  constexpr int GM = MODE == kModeChannel ? 4 : 8;
   const int per_group = GM * tilesN;
   const int first_m = (t / per_group) * GM;
   const int gsz = min(tilesM - first_m, GM);
