@@ -40,8 +40,9 @@
 //   the other half's finished group goes through its epilogue (int32 ->
 //   fp32, FMA with the group's fp16 scale), so the vector ALU work overlaps
 //   the matrix core. Other group sizes apply the epilogue after each group.
-// - Tiles are visited in groups of 8 tile-rows (4 for per-channel weights), and block ids are remapped
-//   so each XCD (own L2) works on a contiguous range of tiles.
+// - Tiles are visited in groups of 8 tile-rows (4 for per-channel weights),
+//   and block ids are remapped so each XCD (own L2) works on a contiguous
+//   range of tiles.
 #include <type_traits>
 
 #include "w4_device.h"
