@@ -75,8 +75,17 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   __shared__ int s_tok[kEM];                                  // token of each tile row (-1: none)
   __shared__ __attribute__((aligned(16))) float s_gs[kEStages][kEM];   // -8 * group sum per staged row
 
-  // ---- work item of this block
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  // ---- work item of this block. Block ids go to the 8 XCDs in turn; XCD x
+  // takes the x-th eighth of the real work items (their count is known only
+  // here), so the idle blocks of the upper-bound grid fall on every XCD
+  // rather than all on the last ones. The host rounds the grid up to a
+  // multiple of 8, which leaves every XCD at least an eighth of it.
+  int total = 0;
+  for (int ee = 0; ee < E; ++ee) total += (offsets[ee + 1] - offsets[ee] + kEM - 1) / kEM * NT;
+  const int per = (total + 7) / 8, xi = (int)(blockIdx.x / 8);
+  if (xi >= per) return;
+  const int t = (int)(blockIdx.x % 8) * per + xi;
+  if (t >= total) return;
   int e = -1, mt = 0, tn = 0, seg0 = 0, cnt = 0;
   {
     int cum = 0;
@@ -376,7 +385,7 @@ hipError_t launch_grouped_fp8(const void* a, const float* a_scale, const float* 
   if (R == 0 || N == 0 || E == 0) return hipSuccess;
   const int KT = (int)(K / kEK), NT = (int)((N + kEN - 1) / kEN);
   const int64_t upper = ((R + kEM - 1) / kEM + E) * NT;
-  dim3 grid((unsigned)upper), block(kEThreads);
+  dim3 grid((unsigned)((upper + 7) / 8 * 8)), block(kEThreads);
   auto Ap = static_cast<const uint8_t*>(a);
   auto Wp = static_cast<const uint8_t*>(w_tiled);
   auto Sp = static_cast<const uint16_t*>(w_scale);
