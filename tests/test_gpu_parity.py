@@ -305,6 +305,23 @@ def test_grouped_small(E, K, N, group, T, topk):
     assert_close(to_f64(y), ref, f"grouped E={E} K={K} N={N}")
 
 
+@pytest.mark.parametrize("counts", [
+    (0, 64, 65, 130, 0, 200, 1),     # empty experts between ragged ones
+    (63, 64, 128, 129, 192, 193)])   # last row tiles of 63, 64, 128, 1, 64 and 65 rows
+def test_grouped_ragged_counts(counts):
+    """Expert row counts around the row tile and its halves (the two waves
+    of a column half each own 64 rows), empty experts included."""
+    counts = np.array(counts)
+    d = W.moe_inputs(len(counts), 256, 136, 128, 256, 1, seed=int(counts.sum()))
+    rng = np.random.default_rng(12)
+    d["row_token"] = rng.integers(0, d["T"], int(counts.sum())).astype(np.int32)
+    d["expert_offsets"] = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a8, s, y = _moe_run(d)
+    rc, rs = O.quantize_act_fp8(O.bf16_bits_to_f32(d["x"]))
+    ref = O.grouped_fp8_reference(rc, rs, d["row_token"], d["expert_offsets"], d["w"], d["scales"], d["group"])
+    assert_close(to_f64(y), ref, f"grouped counts={tuple(counts)}")
+
+
 def test_grouped_moe_workload():
     d = W.named("w4afp8_moe")
     print(f"\n[moe] E={d['E']} T={d['T']} K={d['K']} N={d['N']}", flush=True)
