@@ -10,12 +10,14 @@
 //
 // Design (gfx950):
 // - 256 threads, block tile 128x128, four waves of 64x64, K step 128.
-//   Group 128 and per-channel: three A-only LDS stages (48 KiB), A two K
-//   steps ahead, B straight into registers (one step ahead for group 128,
-//   two for per-channel, in alternating register sets); two blocks per CU
-//   (three for per-channel at 166 VGPRs). Other group sizes: two A+B stages
-//   (64 KiB), loads one step ahead. The int32 partials test hook runs each
-//   of these modes with a store in place of the epilogue.
+//   Group 128: three A-only LDS stages (48 KiB), A two K steps ahead, B
+//   straight into registers one step ahead. Per-channel: three stages of A
+//   and packed B (72 KiB), both by LDS DMA two K steps ahead, so each B
+//   byte passes the vector memory path once per block (that path, not the
+//   matrix core, is what the per-channel kernel waits on). Two blocks per
+//   CU. Other group sizes: two A+B stages (64 KiB), loads one step ahead.
+//   The int32 partials test hook runs each of these modes with a store in
+//   place of the epilogue.
 // - Loads are raw buffer loads. A (int8 codes) goes straight from memory to
 //   LDS, its range check zero-filling rows past M; B is the tiled int4
 //   layout, 8 KiB contiguous per tile.
@@ -27,10 +29,10 @@
 //   low nibbles serve the first 64-deep MFMA step and the high nibbles the
 //   second, and the A fragments carry the same K assignment (chunk 2q +
 //   step, stored where the bank-conflict-free read pattern finds it). That
-//   halves the LDS traffic. Per-channel weights use the same loads; the
-//   int32 accumulators then run over all of K and the column scale is
-//   applied once after the loop. The two-stage modes unpack B once per
-//   block into LDS.
+//   halves the LDS traffic. Per-channel weights are read from their stage
+//   in the same per-lane layout; the int32 accumulators then run over all
+//   of K and the column scale is applied once after the loop. The
+//   two-stage modes unpack B once per block into LDS.
 // - A and B rows in LDS are 128 bytes; 16-byte chunk kc of row r sits at
 //   kc ^ (r & 7). Fragment reads and tile writes are then bank-conflict free
 //   (measured), and every fragment address is a base register plus an
@@ -73,7 +75,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 // the kernel ends after the K loop; loads, unpack, LDS layout, MFMAs and
 // their schedule are the ones the epilogue-fused instantiation runs.
 template <int MODE, bool OUT_BF16, int GC, bool PART>
-__global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel(
+__global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
@@ -86,8 +88,10 @@ __global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel
   constexpr bool kStepScales = kPingPong && MODE != kModeChannel;
   static_assert(MODE != kModeSplit || GC == 2, "split K is built for group 128");
   static_assert(!PART || MODE != kModeSplit, "partials are stored by the unsplit modes");
-  // group 128: three A-only stages (B stays in registers); otherwise two A+B stages
-  constexpr int kSS = kPingPong ? kStageA : kStage;     // bytes per stage
+  // group 128: three A-only stages (B stays in registers); per-channel: three
+  // stages of A and packed B, both by LDS DMA; otherwise two A+B stages
+  constexpr bool kBL = MODE == kModeChannel;
+  constexpr int kSS = kPingPong ? (kBL ? kStageA + kStageB / 2 : kStageA) : kStage;   // bytes per stage
   constexpr int kNS = kPingPong ? 3 : 2;                // stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[kNS * kSS];
   const int group_chunks = GC > 0 ? GC : group_chunks_rt;
@@ -140,8 +144,6 @@ __global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel
   // unit (64 wn + 16 j + l%16, l/16); the 64 lanes cover one KiB per block j
   const uint32_t wd_voff = 64u * (uint32_t)(lane & 15) + 16u * (uint32_t)(lane >> 4) + 4096u * (uint32_t)wn;
   v4i pb[kPingPong ? 4 : 2];
-  // per-channel: B two K steps ahead, alternating between pb and pb2
-  v4i pb2[MODE == kModeChannel ? 4 : 1];
   auto gload_a = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
     const uint32_t ks = (uint32_t)tk * kBK;
@@ -151,13 +153,20 @@ __global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel
           arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (32 * wave_u + 8 * i) * kBK), 16,
           a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
   };
-  auto gload_bd = [&](int tk, auto PBc) {
+  auto gload_bd = [&](int tk) {
     const uint32_t ws = (uint32_t)tk * kTileBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, wd_voff + 1024u * j, ws, 0);
-      if constexpr (decltype(PBc)::value == 0) pb[j] = v; else pb2[j] = v;
-    }
+    for (int j = 0; j < 4; ++j) pb[j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, wd_voff + 1024u * j, ws, 0);
+  };
+  // per-channel: the block's packed B tile (8 KiB, column n's 64 bytes at
+  // 64 n) straight into the stage after A, one KiB per load, two per wave
+  auto gload_bl = [&](int tk, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + kStageA + (2 * wave_u + i) * 1024), 16,
+          16u * (uint32_t)lane + 1024u * (uint32_t)(2 * wave + i), (uint32_t)tk * kTileBytes, 0, 0);
   };
   auto gload = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
@@ -329,14 +338,14 @@ __global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel
     }
   }
   if constexpr (MODE == kModeChannel) {
-    gload_bd(kt0, IC<0>{});
+    gload_bl(kt0, IC<0>{});
     gload_a(kt0, IC<0>{});
-    gload_bd(min(kt0 + 1, kt1 - 1), IC<1>{});
+    gload_bl(min(kt0 + 1, kt1 - 1), IC<1>{});
     gload_a(min(kt0 + 1, kt1 - 1), IC<1>{});
-    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): all but tile 1's B and A
+    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): all but tile 1's B and A
   } else if constexpr (kPingPong) {
     if constexpr (kStepScales) fetch_scales(kt0, scr_cur);
-    gload_bd(kt0, IC<0>{});
+    gload_bd(kt0);
     gload_a(kt0, IC<0>{});
     gload_a(min(kt0 + 1, kt1 - 1), IC<1>{});
     __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): all but tile 1's A
@@ -352,44 +361,48 @@ __global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel
   // stored at the end of the step); with three (group 128) A of tile tk + 2,
   // and B of tile tk + 1 into registers. Past the last tile the loads repeat
   // it, which keeps the body branch-free.
-  auto kstep = [&](int tk, auto STc, auto PBc) {
+  auto kstep = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
-    constexpr int PB = decltype(PBc)::value;   // per-channel: the B buffer of this step
     // direct path: this step's B words (loaded during the previous step)
     // become fragments before the next step's loads reuse the registers.
     // Substep 0 takes the low nibbles (K 32 q + 0..15 of the lane's quarter
     // q), substep 1 the high ones (K 32 q + 16..31); the A fragments follow.
     v4i b0[4], b1[4];
-    if constexpr (kPingPong) {
-      if constexpr (MODE == kModeChannel) {
-        // pin this step's unpack after the previous step's barrier: the
-        // compiler otherwise hoists it two steps up, next to the load of
-        // these words, and waits there for that load to land
+    if constexpr (kBL) {
+      // this wave's 64 columns from the stage: lane (column l%16 of block j,
+      // K quarter l/16) reads its 16-byte unit, the layout the direct loads use
+      const uint8_t* lb = lds + ST * kSS + kStageA + 4096 * wn + 64 * (lane & 15) + 16 * (lane >> 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (PB == 0) asm volatile("" : "+v"(pb[j])); else asm volatile("" : "+v"(pb2[j]));
+      for (int j = 0; j < 4; ++j) {
+        const v4i wv = *reinterpret_cast<const v4i*>(lb + 1024 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = (uint32_t)wv[e];
+          b0[j][e] = (int)((w << 4) & 0xF0F0F0F0u);
+          b1[j][e] = (int)(w & 0xF0F0F0F0u);
         }
       }
+    } else if constexpr (kPingPong) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t w = (uint32_t)(PB == 0 ? pb[j][e] : pb2[j][e]);
+          const uint32_t w = (uint32_t)pb[j][e];
           b0[j][e] = (int)((w << 4) & 0xF0F0F0F0u);
           b1[j][e] = (int)(w & 0xF0F0F0F0u);
         }
     }
     uint32_t scr_next[4];
     if constexpr (MODE == kModeChannel) {
-      // B of tile tk + 2 into the registers just unpacked, then its A: the
-      // step ends waiting for everything but these eight loads
-      gload_bd(min(tk + 2, kt1 - 1), IC<PB>{});
+      // B and A of tile tk + 2 into the stage read at step tk - 1: the step
+      // ends waiting for everything but these six loads
+      gload_bl(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
       gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
     } else if constexpr (kPingPong) {
       // loads in this order, A of tile tk + 2 last, so that the step can end
       // waiting for everything but that: vmcnt(4)
       if constexpr (kStepScales) fetch_scales_split(min(tk + 1, kt1 - 1), scr_next);
-      gload_bd(min(tk + 1, kt1 - 1), IC<0>{});
+      gload_bd(min(tk + 1, kt1 - 1));
       gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
     } else {
       gload(min(tk + 1, KT - 1), IC<ST ^ 1>{});
@@ -469,7 +482,7 @@ __global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel
       lstore_b(IC<ST ^ 1>{});
     }
     if constexpr (MODE == kModeChannel) {
-      __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): tile tk + 2's B and A may stay in flight
+      __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): tile tk + 2's B and A may stay in flight
       barrier_keep_loads();
     } else if constexpr (kPingPong) {
       __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): tile tk + 2's A may stay in flight
@@ -482,36 +495,21 @@ __global__ __launch_bounds__(kGThreads, MODE == 1 ? 3 : 2) void w4a8_gemm_kernel
   };
 
   int tk = kt0;
-  if constexpr (MODE == kModeChannel) {
-    // step i = tk - kt0 reads stage i % 3 and B buffer i % 2
-    for (; tk + 5 < kt1; tk += 6) {
-      kstep(tk, IC<0>{}, IC<0>{});
-      kstep(tk + 1, IC<1>{}, IC<1>{});
-      kstep(tk + 2, IC<2>{}, IC<0>{});
-      kstep(tk + 3, IC<0>{}, IC<1>{});
-      kstep(tk + 4, IC<1>{}, IC<0>{});
-      kstep(tk + 5, IC<2>{}, IC<1>{});
-    }
-    if (tk < kt1) kstep(tk, IC<0>{}, IC<0>{});
-    if (tk + 1 < kt1) kstep(tk + 1, IC<1>{}, IC<1>{});
-    if (tk + 2 < kt1) kstep(tk + 2, IC<2>{}, IC<0>{});
-    if (tk + 3 < kt1) kstep(tk + 3, IC<0>{}, IC<1>{});
-    if (tk + 4 < kt1) kstep(tk + 4, IC<1>{}, IC<0>{});
-  } else if constexpr (kPingPong) {
+  if constexpr (kPingPong) {
     // stage (tk - kt0) % 3; tile tk + 2 streams in while tk is worked on
     for (; tk + 2 < kt1; tk += 3) {
-      kstep(tk, IC<0>{}, IC<0>{});
-      kstep(tk + 1, IC<1>{}, IC<0>{});
-      kstep(tk + 2, IC<2>{}, IC<0>{});
+      kstep(tk, IC<0>{});
+      kstep(tk + 1, IC<1>{});
+      kstep(tk + 2, IC<2>{});
     }
-    if (tk < kt1) kstep(tk, IC<0>{}, IC<0>{});
-    if (tk + 1 < kt1) kstep(tk + 1, IC<1>{}, IC<0>{});
+    if (tk < kt1) kstep(tk, IC<0>{});
+    if (tk + 1 < kt1) kstep(tk + 1, IC<1>{});
   } else {
     for (; tk + 1 < KT; tk += 2) {
-      kstep(tk, IC<0>{}, IC<0>{});
-      kstep(tk + 1, IC<1>{}, IC<0>{});
+      kstep(tk, IC<0>{});
+      kstep(tk + 1, IC<1>{});
     }
-    if (tk < KT) kstep(tk, IC<0>{}, IC<0>{});
+    if (tk < KT) kstep(tk, IC<0>{});
   }
   // the last steps' A tiles may still be streaming into LDS: no wave leaves
   // (or reuses LDS) with its own DMA in flight
