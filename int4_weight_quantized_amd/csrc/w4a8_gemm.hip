@@ -10,29 +10,28 @@
 //
 // Design (gfx950):
 // - 256 threads, block tile 128x128, four waves of 64x64, K step 128.
-//   Group 128: three A-only LDS stages (48 KiB), A two K steps ahead, B
-//   straight into registers one step ahead. Per-channel: three stages of A
-//   and packed B (72 KiB), both by LDS DMA two K steps ahead, so each B
-//   byte passes the vector memory path once per block (that path, not the
-//   matrix core, is what the per-channel kernel waits on). Two blocks per
-//   CU. Other group sizes: two A+B stages (64 KiB), loads one step ahead.
-//   The int32 partials test hook runs each of these modes with a store in
-//   place of the epilogue.
+//   Group 128 and per-channel: three stages of A and packed B (72 KiB), both
+//   by LDS DMA two K steps ahead, so each B byte passes the vector memory
+//   path once per block (that path, not the matrix core, is what the
+//   per-channel kernel waits on; loading B straight into each wave's
+//   registers took it twice, once per wave sharing a column half). Two
+//   blocks per CU. Other group sizes: two A+B stages (64 KiB), loads one
+//   step ahead. The int32 partials test hook runs each of these modes with
+//   a store in place of the epilogue.
 // - Loads are raw buffer loads. A (int8 codes) goes straight from memory to
 //   LDS, its range check zero-filling rows past M; B is the tiled int4
 //   layout, 8 KiB contiguous per tile.
 // - B (stored nibble q^8) becomes int8 bytes 16*(q-8) with a mask (and a
 //   4-bit shift); the MFMA accumulates 16*P and 1/16 is folded into the row
-//   scale (exact). With group 128 each wave loads its own 64 columns straight
-//   into registers, one 16-byte tile unit per lane and column block: lane
-//   (column c, group q) holds the 32 codes of K quarter q of column c, the
-//   low nibbles serve the first 64-deep MFMA step and the high nibbles the
-//   second, and the A fragments carry the same K assignment (chunk 2q +
-//   step, stored where the bank-conflict-free read pattern finds it). That
-//   halves the LDS traffic. Per-channel weights are read from their stage
-//   in the same per-lane layout; the int32 accumulators then run over all
-//   of K and the column scale is applied once after the loop. The
-//   two-stage modes unpack B once per block into LDS.
+//   scale (exact). In the three-stage modes B stays packed in LDS and each
+//   wave reads its own 64 columns, one 16-byte tile unit per lane and
+//   column block: lane (column c, group q) holds the 32 codes of K quarter q
+//   of column c, the low nibbles serve the first 64-deep MFMA step and the
+//   high nibbles the second, and the A fragments carry the same K
+//   assignment (chunk 2q + step, stored where the bank-conflict-free read
+//   pattern finds it). Per-channel, the int32 accumulators run over all of
+//   K and the column scale is applied once after the loop. The two-stage
+//   modes unpack B once per block into LDS.
 // - A and B rows in LDS are 128 bytes; 16-byte chunk kc of row r sits at
 //   kc ^ (r & 7). Fragment reads and tile writes are then bank-conflict free
 //   (measured), and every fragment address is a base register plus an
@@ -81,16 +80,16 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
     int32_t* __restrict__ partials, int M, int N, int K, int KT, int tilesM, int tilesN,
     float* __restrict__ ws, int splits, const float* __restrict__ a_off, const float* __restrict__ w_off) {
-  // B straight into registers with three A-only LDS stages: group 128 (its
-  // epilogue interleaved with the MFMAs) and per-channel (whole K summed in
-  // the int32 accumulators, scales applied once after the loop)
+  // three LDS stages of A and B: group 128 (its epilogue interleaved with
+  // the MFMAs) and per-channel (whole K summed in the int32 accumulators,
+  // scales applied once after the loop)
   constexpr bool kPingPong = ((MODE == kModeGroup || MODE == kModeSplit) && GC == 2) || MODE == kModeChannel;
   constexpr bool kStepScales = kPingPong && MODE != kModeChannel;
   static_assert(MODE != kModeSplit || GC == 2, "split K is built for group 128");
   static_assert(!PART || MODE != kModeSplit, "partials are stored by the unsplit modes");
   // group 128: three A-only stages (B stays in registers); per-channel: three
   // stages of A and packed B, both by LDS DMA; otherwise two A+B stages
-  constexpr bool kBL = MODE == kModeChannel;
+  constexpr bool kBL = kPingPong;
   constexpr int kSS = kPingPong ? (kBL ? kStageA + kStageB / 2 : kStageA) : kStage;   // bytes per stage
   constexpr int kNS = kPingPong ? 3 : 2;                // stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[kNS * kSS];
@@ -140,10 +139,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   const int a_lchunk = kPingPong ? 2 * ((lchunk ^ lrow) & 3) + ((lchunk ^ lrow) >> 2) : (lchunk ^ lrow);
   const uint32_t a_voff = (uint32_t)(32 * wave + lrow) * (uint32_t)K + 16u * (uint32_t)a_lchunk;
   const uint32_t w_voff = 16u * tid;                                               // units tid, tid+256
-  // direct path: lane (column l%16 of 16-column block j, K quarter l/16) loads
-  // unit (64 wn + 16 j + l%16, l/16); the 64 lanes cover one KiB per block j
-  const uint32_t wd_voff = 64u * (uint32_t)(lane & 15) + 16u * (uint32_t)(lane >> 4) + 4096u * (uint32_t)wn;
-  v4i pb[kPingPong ? 4 : 2];
+  v4i pb[2];                                        // two-stage modes: B words on their way to LDS
   auto gload_a = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
     const uint32_t ks = (uint32_t)tk * kBK;
@@ -152,11 +148,6 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (32 * wave_u + 8 * i) * kBK), 16,
           a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
-  };
-  auto gload_bd = [&](int tk) {
-    const uint32_t ws = (uint32_t)tk * kTileBytes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pb[j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, wd_voff + 1024u * j, ws, 0);
   };
   // per-channel: the block's packed B tile (8 KiB, column n's 64 bytes at
   // 64 n) straight into the stage after A, one KiB per load, two per wave
@@ -177,13 +168,8 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
           arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (32 * wave_u + 8 * i) * kBK), 16,
           a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
     const uint32_t ws = (uint32_t)tk * kTileBytes;
-    if constexpr (kPingPong) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pb[j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, wd_voff + 1024u * j, ws, 0);
-    } else {
-      pb[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws, 0);
-      pb[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws + 4096u, 0);
-    }
+    pb[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws, 0);
+    pb[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws + 4096u, 0);
   };
   // B unit u (row n = u/4, K quarter q = u%4): its low nibbles unpack to the
   // logical chunk 2q (K 32q+0..15), its high nibbles to chunk 2q+1.
@@ -345,10 +331,11 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
     __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): all but tile 1's B and A
   } else if constexpr (kPingPong) {
     if constexpr (kStepScales) fetch_scales(kt0, scr_cur);
-    gload_bd(kt0);
+    gload_bl(kt0, IC<0>{});
     gload_a(kt0, IC<0>{});
+    gload_bl(min(kt0 + 1, kt1 - 1), IC<1>{});
     gload_a(min(kt0 + 1, kt1 - 1), IC<1>{});
-    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): all but tile 1's A
+    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): all but tile 1's B and A
   } else {
     gload(0, IC<0>{});
     lstore_b(IC<0>{});
@@ -358,19 +345,19 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
 
   // K step tk reads LDS stage ST while the next tiles stream in: with two
   // stages tile tk + 1 into the other one (A directly, B through registers
-  // stored at the end of the step); with three (group 128) A of tile tk + 2,
-  // and B of tile tk + 1 into registers. Past the last tile the loads repeat
-  // it, which keeps the body branch-free.
+  // stored at the end of the step); with three (group 128, per-channel) A
+  // and B of tile tk + 2 by DMA into the stage read at step tk - 1. Past the
+  // last tile the loads repeat it, which keeps the body branch-free.
   auto kstep = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
-    // direct path: this step's B words (loaded during the previous step)
-    // become fragments before the next step's loads reuse the registers.
-    // Substep 0 takes the low nibbles (K 32 q + 0..15 of the lane's quarter
-    // q), substep 1 the high ones (K 32 q + 16..31); the A fragments follow.
+    // three-stage modes: this step's B words become fragments. Substep 0
+    // takes the low nibbles (K 32 q + 0..15 of the lane's quarter q),
+    // substep 1 the high ones (K 32 q + 16..31); the A fragments follow.
     v4i b0[4], b1[4];
     if constexpr (kBL) {
-      // this wave's 64 columns from the stage: lane (column l%16 of block j,
-      // K quarter l/16) reads its 16-byte unit, the layout the direct loads use
+      // this wave's 64 columns from the stage: lane (column l%16 of 16-column
+      // block j, K quarter l/16) reads unit (64 wn + 16 j + l%16, l/16), the
+      // 64 lanes one contiguous KiB per block (bank-conflict free)
       const uint8_t* lb = lds + ST * kSS + kStageA + 4096 * wn + 64 * (lane & 15) + 16 * (lane >> 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -382,15 +369,6 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
           b1[j][e] = (int)(w & 0xF0F0F0F0u);
         }
       }
-    } else if constexpr (kPingPong) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = (uint32_t)pb[j][e];
-          b0[j][e] = (int)((w << 4) & 0xF0F0F0F0u);
-          b1[j][e] = (int)(w & 0xF0F0F0F0u);
-        }
     }
     uint32_t scr_next[4];
     if constexpr (MODE == kModeChannel) {
@@ -402,7 +380,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       // loads in this order, A of tile tk + 2 last, so that the step can end
       // waiting for everything but that: vmcnt(4)
       if constexpr (kStepScales) fetch_scales_split(min(tk + 1, kt1 - 1), scr_next);
-      gload_bd(min(tk + 1, kt1 - 1));
+      gload_bl(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
       gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
     } else {
       gload(min(tk + 1, KT - 1), IC<ST ^ 1>{});
@@ -485,7 +463,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): tile tk + 2's B and A may stay in flight
       barrier_keep_loads();
     } else if constexpr (kPingPong) {
-      __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): tile tk + 2's A may stay in flight
+      __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): tile tk + 2's B and A may stay in flight
       barrier_keep_loads();
       if constexpr (kStepScales) pair_scales(scr_next, scr_cur);
     } else {
