@@ -18,33 +18,37 @@
 // - The group's fp16 scale is applied with one FMA per output into fp32
 //   accumulators; the token scale at the end.
 // - Block tile 128 rows x 128 columns, 4 waves of 64x64, K step 128, two
-//   blocks per CU (234 VGPRs).
+//   blocks per CU (204 VGPRs, 74 KiB of LDS).
 // - A: activation rows gathered by token id straight into LDS (LDS DMA: each
 //   lane's source row is its token's; rows past the segment read as zero),
 //   three stages. Logical 16-byte chunk 2q + s of a row sits at physical
 //   chunk (4s + q) ^ (row & 7), where lane group q reads it without bank
 //   conflicts.
-// - B: no LDS. Each wave loads its own 64 columns straight into registers,
-//   one step ahead: lane (column c, lane group q) takes the 16-byte tile unit
-//   holding K 32q .. 32q+31 of column c, whose low nibbles are K 32q..+15 and
-//   high nibbles K 32q+16..+31 -- exactly the 32 fp8 bytes the MFMA wants
-//   from that lane, matching the A fragment (logical chunks 2q, 2q+1).
+// - B: the block's packed 8 KiB weight tile of a K step goes into the same
+//   stage as A by LDS DMA, so each weight byte crosses the vector memory
+//   path once per block (loaded straight into registers, each column half
+//   crossed it twice, once per wave using it: 2% slower). Each wave reads
+//   its own 64 columns: lane (column c, lane group q) takes the 16-byte tile
+//   unit holding K 32q .. 32q+31 of column c, whose low nibbles are K
+//   32q..+15 and high nibbles K 32q+16..+31 -- exactly the 32 fp8 bytes the
+//   MFMA wants from that lane, matching the A fragment (logical chunks 2q,
+//   2q+1).
 // - With group 128 (a whole group per K step) the MFMAs are asm statements,
 //   so that they keep their order, and the vector work of the step is placed
-//   between them: block j's four MFMAs carry block j + 1's unpack and reload
-//   and block j - 1's epilogue (left to the compiler, the unpack all came
+//   between them: block j's four MFMAs carry block j + 1's unpack and block
+//   j - 1's epilogue (left to the compiler, the unpack all came
 //   first and the epilogue all last). The stage index and the K offset of the
 //   A DMA are scalar. Other group sizes use the builtin MFMA.
 // - One K step per loop iteration, the stage index in a register. A step
-//   first reads all of its A fragments and C starts (before it issues its
-//   own LDS DMA, so those reads wait for nothing newer than the previous
-//   step's DMA: a tile has one step to arrive), then issues the scales, sums
-//   and A of later steps, and works its four 16-column blocks in turn, each
-//   unpacked as its words are reloaded for the next step; a block's group
-//   epilogue runs under the next block's MFMAs (the last block's under the
-//   next step's first). (Three steps unrolled with constant stage indices
-//   spilled registers; B staged unpacked in LDS, or the DMA issued before
-//   the fragment reads, measured 17% and 13% slower.)
+//   first reads all of its A fragments, B words and C starts (before it
+//   issues its own LDS DMA, so those reads wait for nothing newer than the
+//   previous step's DMA: a tile has one step to arrive), then issues the
+//   scales, sums, A and B of later steps, and works its four 16-column
+//   blocks in turn, each unpacked under the previous one's MFMAs; a block's
+//   group epilogue runs under the next block's MFMAs (the last block's under
+//   the next step's first). (Three steps unrolled with constant stage
+//   indices spilled registers; B staged unpacked in LDS, or the DMA issued
+//   before the fragment reads, measured 17% and 13% slower.)
 // - The group sums of a staged tile sit in LDS beside it; threads 0..127 load
 //   them two steps ahead and store them one step ahead.
 // - Work items (expert, row tile, column tile) are enumerated on the device
@@ -60,6 +64,8 @@ namespace w4 {
 constexpr int kEM = 128, kEN = 128, kEK = 128;
 constexpr int kEThreads = 256;
 constexpr int kEStageA = kEM * kEK;                // 16 KiB
+constexpr int kEStageB = kEN * kEK / 2;            // 8 KiB of packed weights
+constexpr int kESS = kEStageA + kEStageB;          // a stage: A, then B
 constexpr int kEStages = 3;
 
 typedef _Float16 eh2 __attribute__((ext_vector_type(2)));
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     const int32_t* __restrict__ row_token, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ Wt, int64_t w_stride, const uint16_t* __restrict__ wscale,
     uint16_t* __restrict__ out, int N, int K, int KT, int NT, int T) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kEStages * kEStageA];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kEStages * kESS];
   __shared__ int s_tok[kEM];                                  // token of each tile row (-1: none)
   __shared__ __attribute__((aligned(16))) float s_gs[kEStages][kEM];   // -8 * group sum per staged row
 
@@ -135,18 +141,28 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          arsrc, (__attribute__((address_space(3))) void*)(lds + st * kEStageA + (32 * wave_u + 8 * i) * kEK), 16,
+          arsrc, (__attribute__((address_space(3))) void*)(lds + st * kESS + (32 * wave_u + 8 * i) * kEK), 16,
           a_voff[i], ks, 0, 0);
   };
 
-  // ---- B straight into registers: lane (column l%16 of 16-column block j,
-  // lane group l/16) loads unit (64 wn + 16 j + l%16, l/16) of the K tile
+  // ---- B: the block's packed 8 KiB tile of the K step into the stage after
+  // A (LDS DMA, one KiB per load, two per wave), so each weight byte passes
+  // the vector memory path once per block; lane (column l%16 of 16-column
+  // block j, lane group l/16) then reads unit (64 wn + 16 j + l%16, l/16)
   const __amdgpu_buffer_rsrc_t wrsrc =
       make_rsrc(Wt + (int64_t)e * w_stride + (int64_t)tn * KT * kTileBytes, (uint32_t)KT * kTileBytes);
-  const uint32_t wd_voff = 64u * (uint32_t)(lane & 15) + 16u * (uint32_t)(lane >> 4) + 4096u * (uint32_t)wn;
+  auto gload_b = [&](int tk, int st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrsrc, (__attribute__((address_space(3))) void*)(lds + st * kESS + kEStageA + (2 * wave_u + i) * 1024), 16,
+          16u * (uint32_t)lane + 1024u * (uint32_t)(2 * wave + i), (uint32_t)tk * kTileBytes, 0, 0);
+  };
+  const int b_ro = kEStageA + 4096 * wn + 64 * (lane & 15) + 16 * (lane >> 4);
   v4i pb[4];
-  auto gload_b = [&](int tk, int j) {
-    pb[j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, wd_voff + 1024u * j, (uint32_t)tk * kTileBytes, 0);
+  auto read_b = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pb[j] = *reinterpret_cast<const v4i*>(lds + st * kESS + b_ro + 1024 * j);
   };
   // stored q ^ 8 -> fp8 bytes q: low nibbles are K 32q..+15, high K 32q+16..+31
   auto unpack_b = [&](int j) -> v8i {
@@ -231,7 +247,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   const int a_ro0 = (64 * wm + (lane & 15)) * kEK + 16 * (g4 ^ fl);
   const int a_ro1 = (64 * wm + (lane & 15)) * kEK + 16 * ((g4 + 4) ^ fl);
   auto read_a = [&](int st, int i) -> v8i {
-    const uint8_t* base = lds + st * kEStageA + 16 * kEK * i;
+    const uint8_t* base = lds + st * kESS + 16 * kEK * i;
     const v4i x0 = *reinterpret_cast<const v4i*>(base + a_ro0);
     const v4i x1 = *reinterpret_cast<const v4i*>(base + a_ro1);
     return v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
@@ -239,24 +255,24 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   auto read_cinit = [&](int st, int i) -> v4f {
     return *reinterpret_cast<const v4f*>(&s_gs[st][64 * wm + 16 * i + 4 * g4]);
   };
-  // ---- prologue: scales and B of step 0, sums and A of steps 0 and 1
+  // ---- prologue: scales of step 0, B, sums and A of steps 0 and 1
   eh2 sc_cur[2], sc_next[2], sc_prev[2] = {eh2{0, 0}, eh2{0, 0}};
   fetch_scales(0, sc_cur);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) gload_b(0, j);
+  gload_b(0, 0);
   const float gs0 = gload_gs(0);
   gload_a(0, 0);
   float gs_pend = gload_gs(min(1, KT - 1));  // the sums of the step after the current one
+  gload_b(min(1, KT - 1), 1);
   gload_a(min(1, KT - 1), 1);
-  __builtin_amdgcn_s_waitcnt(0x0F75);      // vmcnt(5): all but step 1's sums and A
+  __builtin_amdgcn_s_waitcnt(0x0F77);      // vmcnt(7): all but step 1's sums, B and A
   if (tid < kEM) s_gs[0][tid] = -8.f * gs0;
   __syncthreads();
 
-  // K step tk reads A stage tk % 3 and the B words loaded during step tk - 1.
-  // It issues the scales and B of step tk + 1 and the sums and A of step
-  // tk + 2 (into the stage read at step tk - 1). The step ends once step
-  // tk + 1's A has landed and its sums are stored (the 13 newest loads may
-  // stay in flight across the barrier).
+  // K step tk reads stage tk % 3 (A and B). It issues the scales of step
+  // tk + 1 and the sums, A and B of step tk + 2 (into the stage read at step
+  // tk - 1). The step ends once step tk + 1's A and B have landed and its
+  // sums are stored (the 11 newest loads may stay in flight across the
+  // barrier).
   bool last_prev = false;                  // did the previous step end a group?
   auto kstep = [&](int tk, int st_) {
     const int st = __builtin_amdgcn_readfirstlane(st_);
@@ -271,15 +287,16 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       af[i] = read_a(st, i);
       ci[i] = read_cinit(st, i);
     }
+    read_b(st);
     fetch_scales(tn1, sc_next);
     const float gs_new = gload_gs(min(tk + 2, KT - 1));
     gload_a(min(tk + 2, KT - 1), st == 0 ? 2 : st - 1);
+    gload_b(min(tk + 2, KT - 1), st == 0 ? 2 : st - 1);
     if constexpr (GT == 1) {
       // every step is one whole group: block j's four MFMAs carry block
-      // j + 1's unpack and reload and block j - 1's epilogue between them
+      // j + 1's unpack and block j - 1's epilogue between them
       v8i bf = unpack_b(0);
       asm volatile("" : "+v"(bf)::"memory");
-      gload_b(tn1, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v8i bn = bf;
@@ -291,10 +308,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
           bn = unpack_b(j + 1);
         }
         mfma_fresh(acc[1][j], af[1], bf, ci[1]);
-        if (j < 3) {
-          asm volatile("" : "+v"(bn)::"memory");
-          gload_b(tn1, j + 1);
-        }
+        if (j < 3) asm volatile("" : "+v"(bn)::"memory");
         mfma_fresh(acc[2][j], af[2], bf, ci[2]);
         if (epi) {
           pin_facc(je, 0);
@@ -315,7 +329,6 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
     for (int j = 0; j < 4; ++j) {
       v8i bf = unpack_b(j);
       asm volatile("" : "+v"(bf)::"memory");
-      gload_b(tn1, j);                       // this block's words of the next step
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf, fresh ? ci[i] : acc[i][j], 0, 0, 0,
@@ -333,7 +346,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
       sc_prev[h] = sc_cur[h];
       sc_cur[h] = sc_next[h];
     }
-    __builtin_amdgcn_s_waitcnt(0x0F7D);    // vmcnt(13): step tk + 1's A and sums landed
+    __builtin_amdgcn_s_waitcnt(0x0F7B);    // vmcnt(11): step tk + 1's A, B and sums landed
     if (tid < kEM) s_gs[st == 2 ? 0 : st + 1][tid] = -8.f * gs_pend;
     gs_pend = gs_new;
     __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0): sums stored (vmcnt left as is)
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   // ---- output: row scale, bf16, staged through LDS and written as 16-byte
   // row segments (N is a multiple of 8)
   constexpr int kORow = kEN * 2 + 16;
-  static_assert(kEM * kORow <= kEStages * kEStageA, "output tile fits the stage buffers");
+  static_assert(kEM * kORow <= kEStages * kESS, "output tile fits the stage buffers");
   __syncthreads();
   const int orow0 = 64 * wm + 4 * g4, ocol0 = 64 * wn + (lane & 15);
 #pragma unroll
