@@ -15,9 +15,12 @@
 //   path once per block (that path, not the matrix core, is what the
 //   per-channel kernel waits on; loading B straight into each wave's
 //   registers took it twice, once per wave sharing a column half). Two
-//   blocks per CU. Other group sizes: two A+B stages (64 KiB), loads one
-//   step ahead. The int32 partials test hook runs each of these modes with
-//   a store in place of the epilogue.
+//   blocks per CU. Per-channel shapes with at least 256 blocks of 128 x 256
+//   take those instead: eight waves (2 x 4 of 64x64), 96 KiB of stages, one
+//   block per CU, a third fewer A and B bytes per MFMA. Other group sizes:
+//   two A+B stages (64 KiB), loads one step ahead. The int32 partials test
+//   hook runs each of these modes, in the block shape the GEMM of that size
+//   takes, with a store in place of the epilogue.
 // - Loads are raw buffer loads. A (int8 codes) goes straight from memory to
 //   LDS, its range check zero-filling rows past M; B is the tiled int4
 //   layout, 8 KiB contiguous per tile.
@@ -73,8 +76,10 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 // P[m,g,n] (the accumulator holds 16 P) to partials [M, G, N] instead, and
 // the kernel ends after the K loop; loads, unpack, LDS layout, MFMAs and
 // their schedule are the ones the epilogue-fused instantiation runs.
-template <int MODE, bool OUT_BF16, int GC, bool PART>
-__global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
+// WN: waves along N (per-channel only: 4 makes the block 128 x 256 with
+// eight waves, each B and A byte then feeding twice the MFMAs).
+template <int MODE, bool OUT_BF16, int GC, bool PART, int WN = 2>
+__global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ a_scale,
     const v4i* __restrict__ Wt, const uint16_t* __restrict__ wscale, int group_chunks_rt,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
@@ -87,10 +92,16 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   constexpr bool kStepScales = kPingPong && MODE != kModeChannel;
   static_assert(MODE != kModeSplit || GC == 2, "split K is built for group 128");
   static_assert(!PART || MODE != kModeSplit, "partials are stored by the unsplit modes");
+  static_assert(WN == 2 || (WN == 4 && MODE == kModeChannel), "wide blocks are built for per-channel weights");
+  constexpr int kNT = 128 * WN;                         // threads
+  constexpr int kNW = 2 * WN;                           // waves
+  constexpr int kBNw = 64 * WN;                         // block columns
+  constexpr int kRPW = kBM / kNW;                       // A rows each wave brings into a stage
+
   // group 128: three A-only stages (B stays in registers); per-channel: three
   // stages of A and packed B, both by LDS DMA; otherwise two A+B stages
   constexpr bool kBL = kPingPong;
-  constexpr int kSS = kPingPong ? (kBL ? kStageA + kStageB / 2 : kStageA) : kStage;   // bytes per stage
+  constexpr int kSS = kPingPong ? (kBL ? kStageA + kBNw * kBK / 2 : kStageA) : kStage;   // bytes per stage
   constexpr int kNS = kPingPong ? 3 : 2;                // stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[kNS * kSS];
   const int group_chunks = GC > 0 ? GC : group_chunks_rt;
@@ -112,23 +123,28 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   const int gsz = min(tilesM - first_m, GM);
   const int tm = first_m + (t % per_group) % gsz;
   const int tn = (t % per_group) / gsz;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int m0 = tm * kBM, n0 = tn * kBNw;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int nchunks = (K + 63) >> 6;
   const int G = (MODE == kModeChannel) ? 1 : nchunks / group_chunks;
 
   // ---- global loads: fixed per-lane offsets, K step in the scalar offset.
   // A goes straight to LDS (buffer load with the LDS destination): wave w's
-  // load i fills stage rows 32w + 8i .. +7, one KiB, lane L landing at row
-  // 32w + 8i + L/8, physical 16-byte chunk L%8. The lane fetches the logical
-  // chunk that belongs there under the swizzle p = kc ^ (row & 7); row & 7 is
-  // L/8 for every load, so one per-lane offset serves all four.
+  // load i fills stage rows R w + 8i .. +7 (R = 32, or 16 with eight waves),
+  // one KiB, lane L landing at row R w + 8i + L/8, physical 16-byte chunk
+  // L%8. The lane fetches the logical chunk that belongs there under the
+  // swizzle p = kc ^ (row & 7); row & 7 is L/8 for every load, so one
+  // per-lane offset serves all of them.
   const int rows_valid = min(kBM, M - m0);
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A + (int64_t)m0 * K, (uint32_t)rows_valid * (uint32_t)K);
+  // weights of the block's 128-column tiles (the second of a wide block may
+  // lie past N: its loads then read zeros)
+  const int wtiles = WN == 2 ? 1 : min(2, (N + 127) / 128 - 2 * tn);
   const __amdgpu_buffer_rsrc_t wrsrc =
-      make_rsrc(reinterpret_cast<const uint8_t*>(Wt) + (int64_t)tn * KT * kTileBytes, (uint32_t)KT * kTileBytes);
+      make_rsrc(reinterpret_cast<const uint8_t*>(Wt) + (int64_t)tn * (WN / 2) * KT * kTileBytes,
+                (uint32_t)wtiles * (uint32_t)KT * kTileBytes);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lrow = lane >> 3, lchunk = lane & 7;
   // Group 128 (B in registers) reads logical chunk 2q + s for lane group q
@@ -137,27 +153,32 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   // the fragment reads bank-conflict free. So the lane at physical chunk p
   // fetches logical chunk vinv(p ^ (row & 7)), vinv(u) = 2 (u & 3) + (u >> 2).
   const int a_lchunk = kPingPong ? 2 * ((lchunk ^ lrow) & 3) + ((lchunk ^ lrow) >> 2) : (lchunk ^ lrow);
-  const uint32_t a_voff = (uint32_t)(32 * wave + lrow) * (uint32_t)K + 16u * (uint32_t)a_lchunk;
+  const uint32_t a_voff = (uint32_t)(kRPW * wave + lrow) * (uint32_t)K + 16u * (uint32_t)a_lchunk;
   const uint32_t w_voff = 16u * tid;                                               // units tid, tid+256
   v4i pb[2];                                        // two-stage modes: B words on their way to LDS
   auto gload_a = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
     const uint32_t ks = (uint32_t)tk * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)   // whole offset in the range-checked VGPR operand
+    for (int i = 0; i < kRPW / 8; ++i)   // whole offset in the range-checked VGPR operand
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (32 * wave_u + 8 * i) * kBK), 16,
+          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (kRPW * wave_u + 8 * i) * kBK), 16,
           a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
   };
-  // per-channel: the block's packed B tile (8 KiB, column n's 64 bytes at
-  // 64 n) straight into the stage after A, one KiB per load, two per wave
+  // three-stage modes: the block's packed B tiles (8 KiB per 128 columns,
+  // column n's 64 bytes at 64 n) straight into the stage after A, one KiB
+  // per load, two per wave; KiB u of the stage is KiB u % 8 of 128-column
+  // tile u / 8
   auto gload_bl = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t u = (uint32_t)(2 * wave + i);
+      const uint32_t uo = WN == 2 ? 1024u * u : 1024u * (u & 7u) + (u >> 3) * (uint32_t)KT * kTileBytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wrsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + kStageA + (2 * wave_u + i) * 1024), 16,
-          16u * (uint32_t)lane + 1024u * (uint32_t)(2 * wave + i), (uint32_t)tk * kTileBytes, 0, 0);
+          16u * (uint32_t)lane + uo, (uint32_t)tk * kTileBytes, 0, 0);
+    }
   };
   auto gload = [&](int tk, auto STc) {
     constexpr int ST = decltype(STc)::value;
@@ -165,7 +186,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)   // whole offset in the range-checked VGPR operand
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (32 * wave_u + 8 * i) * kBK), 16,
+          arsrc, (__attribute__((address_space(3))) void*)(lds + ST * kSS + (kRPW * wave_u + 8 * i) * kBK), 16,
           a_voff + (ks + (uint32_t)(8 * i) * (uint32_t)K), 0, 0, 0);
     const uint32_t ws = (uint32_t)tk * kTileBytes;
     pb[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, w_voff, ws, 0);
@@ -552,7 +573,7 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sa[i][r] = a_scale[min(mrow0 + 16 * i + r, M - 1)] * 0.0625f;
-  constexpr int kORow = kBN * 2 + 16;                    // padded output row in LDS, bytes
+  constexpr int kORow = kBNw * 2 + 16;                   // padded output row in LDS, bytes
   static_assert(kBM * kORow <= kNS * kSS, "output tile fits the stage buffers");
   const int orow0 = 64 * wm + 4 * (lane >> 4), ocol0 = 64 * wn + (lane & 15);
   // every wave has drained its A tiles (above) before any overwrites the
@@ -570,8 +591,8 @@ __global__ __launch_bounds__(kGThreads, 2) void w4a8_gemm_kernel(
       }
   __syncthreads();
 #pragma unroll
-  for (int it = 0; it < kBM * kBN / 8 / kGThreads; ++it) {
-    const int c = tid + kGThreads * it, row = c >> 4, seg = c & 15;
+  for (int it = 0; it < kBM * kBNw / 8 / kNT; ++it) {
+    const int c = tid + kNT * it, row = c / (kBNw / 8), seg = c % (kBNw / 8);
     const int m = m0 + row, n = n0 + 8 * seg;
     if (m < M && n < N)
       *reinterpret_cast<v4i*>(out + (int64_t)m * N + n) = *reinterpret_cast<const v4i*>(lds + row * kORow + 16 * seg);
@@ -587,7 +608,12 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
   const int tilesM = (int)((M + kBM - 1) / kBM), tilesN = (int)((N + kBN - 1) / kBN);
   const int nchunks = (int)((K + 63) / 64);
   const int gc = (group == -1) ? nchunks : (int)(group / 64);
+  // per-channel: 128 x 256 blocks of eight waves once they make a full
+  // round of the chip (half the A and B bytes per MFMA)
+  const int tilesNw = (int)((N + 255) / 256);
+  const bool wide = group == -1 && (int64_t)tilesM * tilesNw >= 256;
   dim3 grid((unsigned)(tilesM * tilesN)), block(kGThreads);
+  dim3 grid_w((unsigned)(tilesM * tilesNw)), block_w(2 * kGThreads);
   auto W = static_cast<const v4i*>(w_tiled);
   auto S = static_cast<const uint16_t*>(w_scale);
   auto B = static_cast<const uint16_t*>(bias);
@@ -596,14 +622,22 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
 #define W4A8_LAUNCH(MODE_, BF16_, GC_, PART_)                                                          \
   hipLaunchKernelGGL((w4a8_gemm_kernel<MODE_, BF16_, GC_, PART_>), grid, block, 0, stream, a, a_scale, W, S, gc, \
                      B, O, partials, iM, iN, iK, KT, tilesM, tilesN, nullptr, 1, a_off, w_off)
-  // the partials hook takes the same mode and chunk count as the GEMM
+#define W4A8_LAUNCH_CH(BF16_, PART_)                                                                    \
+  do {                                                                                                  \
+    if (wide)                                                                                           \
+      hipLaunchKernelGGL((w4a8_gemm_kernel<kModeChannel, BF16_, 0, PART_, 4>), grid_w, block_w, 0, stream, a, \
+                         a_scale, W, S, gc, B, O, partials, iM, iN, iK, KT, tilesM, tilesNw, nullptr, 1, a_off, w_off); \
+    else                                                                                                \
+      W4A8_LAUNCH(kModeChannel, BF16_, 0, PART_);                                                       \
+  } while (0)
+  // the partials hook takes the same mode, block shape and chunk count as the GEMM
   if (partials) {
-    if (group == -1) W4A8_LAUNCH(kModeChannel, true, 0, true);
+    if (group == -1) W4A8_LAUNCH_CH(true, true);
     else if (gc == 1) W4A8_LAUNCH(kModeGroup, true, 1, true);
     else if (gc == 2) W4A8_LAUNCH(kModeGroup, true, 2, true);
     else W4A8_LAUNCH(kModeGroup, true, 0, true);
   } else if (group == -1) {
-    if (out_bf16) W4A8_LAUNCH(kModeChannel, true, 0, false); else W4A8_LAUNCH(kModeChannel, false, 0, false);
+    if (out_bf16) W4A8_LAUNCH_CH(true, false); else W4A8_LAUNCH_CH(false, false);
   } else if (gc == 1) {
     if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 1, false); else W4A8_LAUNCH(kModeGroup, false, 1, false);
   } else if (gc == 2) {
@@ -611,6 +645,7 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
   } else {
     if (out_bf16) W4A8_LAUNCH(kModeGroup, true, 0, false); else W4A8_LAUNCH(kModeGroup, false, 0, false);
   }
+#undef W4A8_LAUNCH_CH
 #undef W4A8_LAUNCH
   return hipGetLastError();
 }

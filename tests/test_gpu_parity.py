@@ -166,18 +166,49 @@ def test_partials_bit_exact_edges(M, K, N, group):
     assert np.array_equal(P.cpu().numpy().astype(np.int64), ref["P"])
 
 
-@pytest.mark.parametrize("name,rows", [("w4a8_tiny", None), ("w4a8_up_proj", 64), ("w4a8_down_proj", 64)])
-def test_partials_bit_exact_workloads(name, rows):
+@pytest.mark.parametrize("name,rows,all_rows", [("w4a8_tiny", None, True), ("w4a8_up_proj", 64, False),
+                                                ("w4a8_down_proj", 64, True)])
+def test_partials_bit_exact_workloads(name, rows, all_rows):
+    """Exact int32 group partials against the oracle on a row sample. With
+    all_rows the hook runs on every row, in the block shape the GEMM of that
+    size takes (per-channel at M=8192: the 128 x 256 blocks); the up-
+    projection's group-128 kernel has one block shape, so its sample runs
+    alone."""
     d = W.named(name)
     x, wt, _ = _w4a8_dev(d)
     codes, s, _ = ops.w4a8_quantize_act(x)
     rng = np.random.default_rng(99)
     r = np.arange(d["M"]) if rows is None else np.sort(rng.choice(d["M"], rows, replace=False))
     print(f"\n[partials] {name} rows={len(r)} K={d['K']} N={d['N']}", flush=True)
-    P = ops.w4a8_gemm_partials(codes[torch.from_numpy(r).to(DEV)].contiguous(), wt, d["group"], d["N"])
+    rt = torch.from_numpy(r).to(DEV)
+    if all_rows:
+        P = ops.w4a8_gemm_partials(codes, wt, d["group"], d["N"])[rt]
+    else:
+        P = ops.w4a8_gemm_partials(codes[rt].contiguous(), wt, d["group"], d["N"])
     rc, rs = O.quantize_act_int8(O.half_bits_to_f32(d["x"][r], d["x_dtype"]))
     Pref = O.group_partials(rc, O.unpack_gptq_kn(d["qweight"]), d["group"])
     assert np.array_equal(P.cpu().numpy().astype(np.int64), Pref)
+
+
+@pytest.mark.parametrize("M,K,N", [(2051, 200, 3944), (2176, 1024, 4096)])
+def test_per_channel_wide_blocks(M, K, N):
+    """Per-channel shapes with at least 256 blocks of 128 x 256 (the wide
+    kernel): ragged rows, a ragged K step, and a last block whose second
+    128-column weight tile lies past N; exact partials and outputs on a row
+    sample (first and last rows included)."""
+    d = W.w4a8_inputs(M, K, N, -1, "bf16", seed=M + K + N, with_bias=True)
+    x, wt, sc = _w4a8_dev(d)
+    bias = dev_half(d["bias"], "bf16")
+    codes, s, _ = ops.w4a8_quantize_act(x)
+    P = ops.w4a8_gemm_partials(codes, wt, -1, N)
+    y = ops.w4a8_gemm(codes, s, wt, sc, -1, N, out_dtype=x.dtype, bias=bias)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    r = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 40, replace=False)]))
+    ref = O.w4a8_reference(d["x"], "bf16", d["qweight"], d["scales"], -1, bias_bits=d["bias"], rows=r)
+    rt = torch.from_numpy(r).to(DEV)
+    assert np.array_equal(P[rt].cpu().numpy().astype(np.int64), ref["P"])
+    assert_close(to_f64(y[rt]), ref["y"], f"wide per-channel {M}x{K}x{N}")
 
 
 @pytest.mark.parametrize("M,K,N,group", EDGE_SHAPES)
