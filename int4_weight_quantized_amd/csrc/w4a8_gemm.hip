@@ -98,10 +98,10 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
   constexpr int kBNw = 64 * WN;                         // block columns
   constexpr int kRPW = kBM / kNW;                       // A rows each wave brings into a stage
 
-  // group 128: three A-only stages (B stays in registers); per-channel: three
-  // stages of A and packed B, both by LDS DMA; otherwise two A+B stages
+  // group 128 and per-channel: three stages of A and packed B, both by LDS
+  // DMA; otherwise two stages of A and unpacked B
   constexpr bool kBL = kPingPong;
-  constexpr int kSS = kPingPong ? (kBL ? kStageA + kBNw * kBK / 2 : kStageA) : kStage;   // bytes per stage
+  constexpr int kSS = kBL ? kStageA + kBNw * kBK / 2 : kStage;   // bytes per stage
   constexpr int kNS = kPingPong ? 3 : 2;                // stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[kNS * kSS];
   const int group_chunks = GC > 0 ? GC : group_chunks_rt;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
                 (uint32_t)wtiles * (uint32_t)KT * kTileBytes);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lrow = lane >> 3, lchunk = lane & 7;
-  // Group 128 (B in registers) reads logical chunk 2q + s for lane group q
+  // The three-stage modes read logical chunk 2q + s for lane group q
   // and step s; it is stored at physical chunk (4s + q) ^ (row & 7), the
   // position the two-stage path reads for its own chunk 4s + q, which keeps
   // the fragment reads bank-conflict free. So the lane at physical chunk p
@@ -331,8 +331,8 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
     }
   };
 
-  // ---- prologue: tile 0 to LDS stage 0 (group 128: tiles 0 and 1 to stages
-  // 0 and 1, and B of tile 0 to registers)
+  // ---- prologue: tile 0 to LDS stage 0 (three-stage modes: tiles 0 and 1
+  // to stages 0 and 1)
   h2 scr_cur[2] = {h2{0, 0}, h2{0, 0}}, scr_prev[2] = {h2{0, 0}, h2{0, 0}};
   if constexpr (MODE == kModeSplit) {
     if (kt0 >= kt1) {                              // an empty split (the host avoids them): zeros
