@@ -168,10 +168,13 @@ __global__ __launch_bounds__(kEThreads, 2) void grouped_fp8_kernel(
   auto unpack_b = [&](int j) -> v8i {
     v8i bf;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t w = (uint32_t)pb[j][c];
-      bf[c] = (int)((w ^ 0x88888888u) & 0x0F0F0F0Fu);
-      bf[4 + c] = (int)(((w >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu);
+    for (int c = 0; c < 4; c += 2) {
+      const uint32_t w0 = (uint32_t)pb[j][c], w1 = (uint32_t)pb[j][c + 1];
+      const uint64_t h = shr64<4>(as_u64x2(pb[j])[c / 2]);   // the high nibbles of both words
+      bf[c] = (int)((w0 ^ 0x88888888u) & 0x0F0F0F0Fu);
+      bf[c + 1] = (int)((w1 ^ 0x88888888u) & 0x0F0F0F0Fu);
+      bf[4 + c] = (int)(((uint32_t)h ^ 0x08080808u) & 0x0F0F0F0Fu);
+      bf[5 + c] = (int)(((uint32_t)(h >> 32) ^ 0x08080808u) & 0x0F0F0F0Fu);
     }
     return bf;
   };

@@ -68,6 +68,30 @@ __device__ __forceinline__ T wave_max(T v) {
 // The memory clobber keeps the compiler from moving memory accesses across.
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
+// A pair of 32-bit words (lo in the lower register) shifted as one 64-bit
+// value by a constant: one v_lshlrev_b64 / v_lshrrev_b64 where two 32-bit
+// shifts would otherwise be issued (the compiler splits a 64-bit shift whose
+// crossing bits are masked off later; the empty asm statement takes the
+// whole 64-bit result, so the shift stays whole and is still an instruction
+// the compiler schedules and checks for hazards itself). The nibble unpacks
+// use them on word pairs: the bits carried across the word boundary land
+// where their masks clear. Pairs come from a 16-byte vector reinterpreted
+// as two 64-bit lanes, so no instruction builds them.
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u64x2 as_u64x2(v4i v) { return __builtin_bit_cast(u64x2, v); }
+template <int N>
+__device__ __forceinline__ uint64_t shl64(uint64_t v) {
+  uint64_t r = v << N;
+  asm("" : "+v"(r));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ uint64_t shr64(uint64_t v) {
+  uint64_t r = v >> N;
+  asm("" : "+v"(r));
+  return r;
+}
+
 // Map a linear block id to a tile id so that blocks the hardware sends to
 // the same XCD (round-robin over 8 XCDs) get a contiguous run of tile ids.
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {

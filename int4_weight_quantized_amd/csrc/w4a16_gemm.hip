@@ -60,14 +60,21 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask_s, uint32_t
   return (a & mask_s) | magic_v;
 }
 
-// word -> 4 registers of bf16 pairs 128+q, K order (see the tiled layout)
-__device__ __forceinline__ v4i unpack_bf16_128q(uint32_t w, uint32_t mask_s, uint32_t magic_v) {
-  v4i r;
-  r[0] = (int)and_or(w, mask_s, magic_v);
-  r[1] = (int)and_or(w >> 4, mask_s, magic_v);
-  r[2] = (int)and_or(w >> 8, mask_s, magic_v);
-  r[3] = (int)and_or(w >> 12, mask_s, magic_v);
-  return r;
+// two words -> 4 registers each of bf16 pairs 128+q, K order (see the tiled
+// layout): word w gives ((w >> 4i) & 0x000F000F) | 0x43004300, i = 0..3;
+// each shift is one 64-bit shift of the pair (the bits carried into the low
+// word land where the mask clears them)
+__device__ __forceinline__ void unpack2_bf16_128q(uint64_t w01, uint32_t mask_s, uint32_t magic_v, v4i& r0, v4i& r1) {
+  const uint32_t w0 = (uint32_t)w01, w1 = (uint32_t)(w01 >> 32);
+  const uint64_t s4 = shr64<4>(w01), s8 = shr64<8>(w01), s12 = shr64<12>(w01);
+  r0[0] = (int)and_or(w0, mask_s, magic_v);
+  r1[0] = (int)and_or(w1, mask_s, magic_v);
+  r0[1] = (int)and_or((uint32_t)s4, mask_s, magic_v);
+  r1[1] = (int)and_or((uint32_t)(s4 >> 32), mask_s, magic_v);
+  r0[2] = (int)and_or((uint32_t)s8, mask_s, magic_v);
+  r1[2] = (int)and_or((uint32_t)(s8 >> 32), mask_s, magic_v);
+  r0[3] = (int)and_or((uint32_t)s12, mask_s, magic_v);
+  r1[3] = (int)and_or((uint32_t)(s12 >> 32), mask_s, magic_v);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -170,14 +177,12 @@ __global__ __launch_bounds__(kDThreads * WPW, 1) void w4a16_kernel(
       v4f c = z4;
 #pragma unroll
       for (int i = 0; i < UPW; ++i) {
-        const uint32_t w0 = (uint32_t)wv[t][i >> 1][(i & 1) * 2];
-        const uint32_t w1 = (uint32_t)wv[t][i >> 1][(i & 1) * 2 + 1];
         // c = sum_k x*(128+q) - 136*XS = sum_k x*(q-8) over the group
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]),
-                                                    as_v8bf(unpack_bf16_128q(w0, mask_s, magic_v)),
+        v4i u0, u1;
+        unpack2_bf16_128q(as_u64x2(wv[t][i >> 1])[i & 1], mask_s, magic_v, u0, u1);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][0]), as_v8bf(u0),
                                                     first_of_group(i) ? xinit[i / UPG] : c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]),
-                                                    as_v8bf(unpack_bf16_128q(w1, mask_s, magic_v)), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(xa[i][1]), as_v8bf(u1), c, 0, 0, 0);
         if (last_of_group(i)) {
           const int gi = i / UPG;                      // local group slot
           const uint32_t sz = (uint32_t)szv[t][gi >> 2][gi & 3];

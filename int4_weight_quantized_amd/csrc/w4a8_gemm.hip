@@ -387,8 +387,7 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
         for (int e = 0; e < 4; e += 2) {
           // two words shifted as one 64-bit value: the nibble carried across
           // the word boundary lands in bits the mask clears
-          uint64_t w2;
-          asm("v_lshlrev_b64 %0, 4, %1" : "=v"(w2) : "v"((uint64_t)(uint32_t)wv[e + 1] << 32 | (uint32_t)wv[e]));
+          const uint64_t w2 = shl64<4>(as_u64x2(wv)[e / 2]);
           b0[j][e] = (int)((uint32_t)w2 & 0xF0F0F0F0u);
           b0[j][e + 1] = (int)((uint32_t)(w2 >> 32) & 0xF0F0F0F0u);
           b1[j][e] = (int)((uint32_t)wv[e] & 0xF0F0F0F0u);
