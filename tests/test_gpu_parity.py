@@ -659,6 +659,26 @@ def test_w4a8_asym_gemm(M, K, N, group, out_dtype):
     assert_close(to_f64(y), ref["y"], f"w4a8 asym {M}x{K}x{N} g{group} {out_dtype}")
 
 
+def test_w4a8_asym_per_channel_wide_rows():
+    """Asymmetric activations with per-channel weights at a size that takes
+    the 128 x 256 blocks (shifted activations, fp16, bias); the oracle on a
+    row sample with the first and last rows."""
+    M, K, N = 2176, 1024, 4096
+    d = W.w4a8_inputs(M, K, N, -1, "f16", seed=31, with_bias=True)
+    x, wt, sc = _w4a8_dev(d)
+    xs = (x.float() + 1.5).to(x.dtype)
+    xs_bits = xs.view(torch.int16).cpu().numpy().view(np.uint16)
+    codes, s, z = ops.w4a8_quantize_act_asym(xs)
+    woff = ops.w4a8_weight_offsets(wt, sc, -1, K, N)
+    bias = dev_half(d["bias"], "f16")
+    y = ops.w4a8_gemm_asym(codes, s, z, wt, sc, -1, woff, N, out_dtype=xs.dtype, bias=bias)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(9).choice(M, 30, replace=False)]))
+    ref = O.w4a8_reference_asym(xs_bits, "f16", d["qweight"], d["scales"], -1, bias_bits=d["bias"], rows=rows)
+    assert np.array_equal(codes.cpu().numpy()[rows], ref["codes"][rows])
+    assert_close(to_f64(y[torch.from_numpy(rows).to(DEV)]), ref["y"], "w4a8 asym per-channel wide")
+
+
 def test_w4a8_asym_up_proj_rows():
     """The up-projection workload with asymmetric activations, at full size;
     the oracle on a row sample."""
