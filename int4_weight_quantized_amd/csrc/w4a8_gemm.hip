@@ -97,6 +97,11 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
   constexpr int kNW = 2 * WN;                           // waves
   constexpr int kBNw = 64 * WN;                         // block columns
   constexpr int kRPW = kBM / kNW;                       // A rows each wave brings into a stage
+  // loads a wave issues for one three-stage K step: A (kRPW / 8 DMAs of 8
+  // rows) and B (2 DMAs); the step's closing wait leaves exactly these in
+  // flight (vmcnt), so everything older, the next step's tiles, has landed
+  constexpr int kStepLoads = kRPW / 8 + 2;
+  static_assert(kStepLoads < 16, "vmcnt immediate");
 
   // group 128 and per-channel: three stages of A and packed B, both by LDS
   // DMA; otherwise two stages of A and unpacked B
@@ -349,14 +354,14 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
     gload_a(kt0, IC<0>{});
     gload_bl(min(kt0 + 1, kt1 - 1), IC<1>{});
     gload_a(min(kt0 + 1, kt1 - 1), IC<1>{});
-    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): all but tile 1's B and A
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kStepLoads);   // all but tile 1's B and A
   } else if constexpr (kPingPong) {
     if constexpr (kStepScales) fetch_scales(kt0, scr_cur);
     gload_bl(kt0, IC<0>{});
     gload_a(kt0, IC<0>{});
     gload_bl(min(kt0 + 1, kt1 - 1), IC<1>{});
     gload_a(min(kt0 + 1, kt1 - 1), IC<1>{});
-    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): all but tile 1's B and A
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kStepLoads);   // all but tile 1's B and A
   } else {
     gload(0, IC<0>{});
     lstore_b(IC<0>{});
@@ -398,12 +403,12 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
     uint32_t scr_next[4];
     if constexpr (MODE == kModeChannel) {
       // B and A of tile tk + 2 into the stage read at step tk - 1: the step
-      // ends waiting for everything but these six loads
+      // ends waiting for everything but these kStepLoads loads
       gload_bl(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
       gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
     } else if constexpr (kPingPong) {
-      // loads in this order, A of tile tk + 2 last, so that the step can end
-      // waiting for everything but that: vmcnt(4)
+      // loads in this order, B and A of tile tk + 2 last, so that the step
+      // can end waiting for everything but those kStepLoads loads
       if constexpr (kStepScales) fetch_scales_split(min(tk + 1, kt1 - 1), scr_next);
       gload_bl(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
       gload_a(min(tk + 2, kt1 - 1), IC<(ST + 2) % 3>{});
@@ -485,10 +490,10 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? 1 : 2) void w4a8_gemm_kernel(
       lstore_b(IC<ST ^ 1>{});
     }
     if constexpr (MODE == kModeChannel) {
-      __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): tile tk + 2's B and A may stay in flight
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kStepLoads);   // tile tk + 2's B and A may stay in flight
       barrier_keep_loads();
     } else if constexpr (kPingPong) {
-      __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): tile tk + 2's B and A may stay in flight
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kStepLoads);   // tile tk + 2's B and A may stay in flight
       barrier_keep_loads();
       if constexpr (kStepScales) pair_scales(scr_next, scr_cur);
     } else {
