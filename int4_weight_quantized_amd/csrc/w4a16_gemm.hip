@@ -39,6 +39,12 @@
 //   unpack overlap the next tile's transfer; issuing every tile at once made
 //   all of them arrive late together. Partial tiles of the 16 waves are
 //   summed through LDS.
+// - Up to 4 rows over K <= 4096 (decode at batch 1-4, the tied output head)
+//   take w4a16_tile_kernel instead: one row tile per block and one window
+//   per wave, every block resident at once and every load issued up front,
+//   activations staged per wave in LDS and their group sums taken on the
+//   vector ALU (no MFMA against ones). Without a chain of tiles, the work
+//   left once a wave's bytes land is a single window's.
 #include "w4_device.h"
 
 namespace w4 {
@@ -51,6 +57,7 @@ constexpr int kWTile = 4096;               // weight bytes per (row tile, window
 constexpr int kSZTile = 16 * 8 * 2 * 2;    // scale/zero bytes per (row tile, window)
 
 __device__ __forceinline__ v8bf as_v8bf(v4i v) { return __builtin_bit_cast(v8bf, v); }
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // (a & mask) | magic in one v_and_or_b32. gfx9 VOP3 encodes no literal and
 // reads at most one scalar operand, so the caller keeps the mask in an SGPR
@@ -212,6 +219,136 @@ __global__ __launch_bounds__(kDThreads * WPW, 1) void w4a16_kernel(
   }
 }
 
+// Few rows (M <= 4) over K <= 4096 (at most 8 windows): one row tile per
+// block, one window per wave (NWV = 4 waves for K <= 2048, else 8). Every
+// block is resident at once (<= 64 VGPRs), and each wave issues all of its
+// loads up front -- its activation rows, then its scale/zero pairs, then
+// its 4 KiB of weights -- so the matrix is requested in a single pass with
+// no chain of tiles behind any block, and the work left once a wave's
+// bytes land is one window's. The activation rows arrive one 16-byte piece
+// per lane (8 consecutive K of a row); from them the wave takes the group
+// sums XS (dot products with ones, a butterfly over the lanes of a group,
+// read out as wave-uniform values) and stages the rows in its own LDS
+// region, from which each unit's A fragments are read as the weights
+// arrive (lanes of rows past M read a zero block). A group's accumulator
+// starts at zero and its epilogue folds the -136 offset into the zero
+// point: y += scale*C + (zero - 136*scale)*XS. A wave whose window is past
+// KW reads nothing (offsets past the buffers load zero, whose share is zero).
+template <int UPG, int MV, int NWV>
+__global__ __launch_bounds__(64 * NWV, 32 / NWV) void w4a16_tile_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wt, const uint8_t* __restrict__ szt,
+    uint16_t* __restrict__ out, int M, int N, int K, int NT16, int KW) {
+  constexpr int NG = 8 / UPG;                 // groups per window
+  constexpr int NSZ = (NG + 3) / 4;           // 16-byte scale/zero registers per window
+  constexpr int kXRow = 1024 + 16;            // LDS bytes per staged row (512 K, padded)
+  constexpr int kXWave = MV * kXRow + 16;     // a wave's rows, then its zero block
+  __shared__ __attribute__((aligned(16))) uint8_t xl[NWV * kXWave];
+  __shared__ __attribute__((aligned(16))) float red[NWV][16][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, j = lane >> 4;
+  const int rt = blockIdx.x;
+  const int kw = __builtin_amdgcn_readfirstlane(wave);     // this wave's window
+  const bool have = kw < KW;
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, (uint32_t)((int64_t)NT16 * KW * kWTile));
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(szt, (uint32_t)((int64_t)NT16 * KW * kSZTile));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+  constexpr uint32_t kPast = 0x80000000u;     // an offset past every buffer: loads zero
+
+  // ---- every load of the wave: activations, scale/zero pairs, weights
+  v4i xv[MV], szv[NSZ], wv[4];
+#pragma unroll
+  for (int m = 0; m < MV; ++m)
+    xv[m] = buffer_load16(xr, have ? (uint32_t)(m * K + kw * kWinK + 8 * lane) * 2u : kPast);
+  {
+    const uint32_t base = have ? (uint32_t)(rt * KW + kw) * kSZTile + 32u * l16 : kPast;
+#pragma unroll
+    for (int q = 0; q < NSZ; ++q) szv[q] = buffer_load16(sr, base + 16u * q);
+  }
+  {
+    const uint32_t base = have ? (uint32_t)(rt * KW + kw) * kWTile + 16u * lane : kPast;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) wv[p] = buffer_load16(wr, base + 1024u * p);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- group sums of the activation rows: lane L holds K 8L .. 8L+7 of the
+  // window, so a group is 8*UPG lanes; XS of group g, row m ends up uniform
+  // in xsum[m][g]
+  float xsum[MV][NG];
+  {
+    const v2bf one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // through a scalar copy: a bit cast straight from the vector
+        // element reads element 0 whatever q is (hipcc 7.2)
+        const uint32_t w2 = (uint32_t)xv[m][q];
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w2), one2, t, false);
+      }
+#pragma unroll
+      for (int off = 1; off < 8 * UPG; off <<= 1) t += __shfl_xor(t, off, kWave);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) xsum[m][g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 8 * UPG * g));
+    }
+  }
+
+  // ---- stage the activation rows in the wave's LDS region (row m at
+  // m*kXRow), and its zero block
+  uint8_t* xw = xl + kw * kXWave;
+#pragma unroll
+  for (int m = 0; m < MV; ++m) *reinterpret_cast<v4i*>(xw + m * kXRow + 16 * lane) = xv[m];
+  if (lane == 0) *reinterpret_cast<v4i*>(xw + MV * kXRow) = v4i{0, 0, 0, 0};
+  // A fragment of unit i, half h: row l16, K 64i + 16j + 8h .. +7
+  const int a_lane = l16 < MV ? l16 * kXRow + 32 * j : -1;
+  auto read_a = [&](int i, int h) -> v4i {
+    const int off = a_lane >= 0 ? a_lane + 128 * i + 16 * h : MV * kXRow;
+    return *reinterpret_cast<const v4i*>(xw + off);
+  };
+
+  const v4f z4 = {0.f, 0.f, 0.f, 0.f};
+  uint32_t mask_s, magic_v;
+  asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(mask_s));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic_v));
+  float y[MV];
+#pragma unroll
+  for (int r = 0; r < MV; ++r) y[r] = 0.f;
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    v4f c = z4;                                // sum_k x*(128+q) over the group
+#pragma unroll
+    for (int ii = 0; ii < UPG; ++ii) {
+      const int i = g * UPG + ii;
+      const v4i a0 = read_a(i, 0), a1 = read_a(i, 1);
+      v4i u0, u1;
+      unpack2_bf16_128q(as_u64x2(wv[i >> 1])[i & 1], mask_s, magic_v, u0, u1);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(a0), as_v8bf(u0), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(a1), as_v8bf(u1), c, 0, 0, 0);
+    }
+    const uint32_t sz = (uint32_t)szv[g >> 2][g & 3];
+    const float s_ = bf16_lo(sz), zc = fmaf(-136.f, s_, bf16_hi(sz));
+#pragma unroll
+    for (int r = 0; r < MV; ++r) y[r] = fmaf(s_, c[r], fmaf(zc, xsum[r][g], y[r]));
+  }
+
+  // ---- the waves' partial sums: rows m < 4 sit in lanes 0-15, register m
+  if (lane < 16) {
+#pragma unroll
+    for (int r = 0; r < MV; ++r) red[wave][lane][r] = y[r];
+  }
+  __syncthreads();
+  if (tid < 16 * M) {
+    const int m = tid >> 4, nn = tid & 15, n = 16 * rt + nn;
+    float acc = 0.f;
+#pragma unroll
+    for (int w_ = 0; w_ < NWV; ++w_) acc += red[w_][nn][m];
+    if (n < N) out[(int64_t)m * N + n] = f32_to_bf16_rne(acc);
+  }
+}
+
 // ---------------------------------------------------------------- repack
 
 __device__ __forceinline__ uint32_t p5_code(const uint8_t* w, int N, int K, int n, int k) {
@@ -282,11 +419,44 @@ hipError_t launch_w4a16_repack(const uint8_t* w, const void* scale, const void* 
   return hipGetLastError();
 }
 
+static hipError_t launch_w4a16_tile(const void* x, const void* w_tiled, const void* sz_tiled, int upg, void* out,
+                                    int64_t M, int64_t N, int64_t K, int NT16, int KW, hipStream_t stream) {
+  auto X = static_cast<const uint16_t*>(x);
+  auto Wt = static_cast<const uint8_t*>(w_tiled);
+  auto St = static_cast<const uint8_t*>(sz_tiled);
+  auto O = static_cast<uint16_t*>(out);
+  const int iM = (int)M, iN = (int)N, iK = (int)K;
+  const int mv = M == 1 ? 1 : (M == 2 ? 2 : 4);
+  const bool eight = KW > 4;
+#define W4A16T_LAUNCH(UPG_, MV_, NWV_)                                                                     \
+  hipLaunchKernelGGL((w4a16_tile_kernel<UPG_, MV_, NWV_>), dim3(NT16), dim3(64 * NWV_), 0, stream, X, Wt, St, O, iM, \
+                     iN, iK, NT16, KW)
+#define W4A16T_NWV(UPG_, MV_)                                            \
+  { if (eight) W4A16T_LAUNCH(UPG_, MV_, 8); else W4A16T_LAUNCH(UPG_, MV_, 4); }
+#define W4A16T_MV(UPG_)                                  \
+  switch (mv) {                                          \
+    case 1: W4A16T_NWV(UPG_, 1) break;                   \
+    case 2: W4A16T_NWV(UPG_, 2) break;                   \
+    default: W4A16T_NWV(UPG_, 4) break;                  \
+  }
+  switch (upg) {
+    case 1: W4A16T_MV(1) break;
+    case 2: W4A16T_MV(2) break;
+    case 4: W4A16T_MV(4) break;
+    default: W4A16T_MV(8) break;
+  }
+#undef W4A16T_MV
+#undef W4A16T_NWV
+#undef W4A16T_LAUNCH
+  return hipGetLastError();
+}
+
 hipError_t launch_w4a16(const void* x, const void* w_tiled, const void* sz_tiled, int64_t group, void* out,
                         int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int NT16 = (int)((N + 15) / 16), KW = (int)((K + kWinK - 1) / kWinK);
   const int upg = (int)(group / 64);
+  if (M <= 4 && KW <= 8) return launch_w4a16_tile(x, w_tiled, sz_tiled, upg, out, M, N, K, NT16, KW, stream);
   // row tiles per block: enough blocks to cover ~all CUs, at most 4 tiles each
   int rt = (NT16 + 255) / 256;
   rt = rt <= 1 ? 1 : (rt == 2 ? 2 : 4);

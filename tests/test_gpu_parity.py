@@ -300,7 +300,10 @@ def test_w4a16_decode_workload(M):
 @pytest.mark.parametrize("M,K,N,group,zero", [
     (16, 64, 8, 64, True), (3, 192, 24, 64, True), (2, 512, 136, 128, True), (1, 256, 40, 256, False),
     (13, 14336, 64, 64, True), (8, 4096, 1000, 64, True), (4, 1536, 72, 512, True), (5, 8192, 4104, 128, True),
-    (1, 512, 9000, 64, True), (8, 256, 16392, 128, True), (2, 1024, 7176, 256, False)])
+    (1, 512, 9000, 64, True), (8, 256, 16392, 128, True), (2, 1024, 7176, 256, False),
+    # one row tile per block (M <= 4, K <= 4096): two windows per wave, a
+    # partial last window, a wave with no second window, four rows
+    (1, 3200, 200, 64, True), (2, 4096, 136, 128, False), (4, 2560, 264, 256, True), (3, 3584, 40, 64, True)])
 def test_w4a16_edges(M, K, N, group, zero):
     d = W.w4a16_inputs(M, K, N, group, seed=M + K + N)
     y = _w4a16_run(d, with_zero=zero)
