@@ -303,7 +303,9 @@ def test_w4a16_decode_workload(M):
     (1, 512, 9000, 64, True), (8, 256, 16392, 128, True), (2, 1024, 7176, 256, False),
     # one row tile per block (M <= 4, K <= 4096): two windows per wave, a
     # partial last window, a wave with no second window, four rows
-    (1, 3200, 200, 64, True), (2, 4096, 136, 128, False), (4, 2560, 264, 256, True), (3, 3584, 40, 64, True)])
+    (1, 3200, 200, 64, True), (2, 4096, 136, 128, False), (4, 2560, 264, 256, True), (3, 3584, 40, 64, True),
+    # two row tiles per block (5 to 8 rows), an odd tile count
+    (6, 2048, 264, 128, True), (7, 4096, 40, 256, False), (5, 1536, 1032, 64, True)])
 def test_w4a16_edges(M, K, N, group, zero):
     d = W.w4a16_inputs(M, K, N, group, seed=M + K + N)
     y = _w4a16_run(d, with_zero=zero)
