@@ -102,6 +102,19 @@ int w4a8_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t 
                       float* group_sums, int64_t group, void* stream);
 
 /*
+ * Test hook of the FP8 encode inside w4a8_quantize_act (W4_FP8_E4M3): the
+ * fp32 values whose bit patterns are first_bits, first_bits + 1, ...,
+ * first_bits + n - 1 are clamped to +-448 and converted to E4M3 (nearest
+ * even) exactly as the quantizer converts its quotients x / s. [w4afp8]
+ * W4AFP8Config: per-token dynamic 8-bit float activations. It lets a test
+ * compare the conversion with a reference on every fp32 input.
+ *   n         a multiple of 8, first_bits + n <= 2^32
+ *   codes     device, n bytes, 8-byte aligned
+ * Non-finite inputs: unspecified codes. Errors: INVALID, ALIGN, HIP.
+ */
+int w4_fp8_encode_range(uint32_t first_bits, int64_t n, uint8_t* codes, void* stream);
+
+/*
  * The same quantization with a static input scale instead of the per-token
  * one. [ct_w4a8] CompressedTensorsW4A8Int takes is_static_input_scheme: a
  * calibrated, per-tensor activation scale fixed at load time. Every row uses

@@ -22,6 +22,7 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
                             const float* a_off = nullptr, const float* w_off = nullptr);
 hipError_t launch_quant_act_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, void* codes,
                                  float* scales, float* offsets, hipStream_t stream);
+hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* codes, hipStream_t stream);
 hipError_t launch_weight_offsets(const void* w_tiled, const void* w_scale, int64_t group, int64_t K, int64_t N,
                                  float* out, hipStream_t stream);
 void w4a16_tiled_bytes(int64_t K, int64_t N, size_t* wbytes, size_t* szbytes);
@@ -103,7 +104,7 @@ extern "C" {
 
 const char* w4_last_error(void) { return g_err; }
 
-int w4_version(void) { return 101; }
+int w4_version(void) { return 102; }
 
 static int quantize_act(const char* fn, const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, void* codes,
                         int code_dtype, float* scales, float* group_sums, int64_t group, const float* static_scale,
@@ -662,6 +663,18 @@ static int nibbles(const char* fn, const uint8_t* src, int64_t N, int64_t K, uin
   if (!src || !dst) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
   if (!aligned16(src) || !aligned16(dst)) return fail(W4_ERR_ALIGN, "%s: buffers must be 16-byte aligned", fn);
   return hip_status(w4::launch_nibbles(src, dst, N, K, pack, static_cast<hipStream_t>(stream)), fn);
+}
+
+int w4_fp8_encode_range(uint32_t first_bits, int64_t n, uint8_t* codes, void* stream) {
+  const char* fn = "w4_fp8_encode_range";
+  if (n < 0) return fail(W4_ERR_INVALID, "%s: negative n=%lld", fn, (long long)n);
+  if (n % 8) return fail(W4_ERR_ALIGN, "%s: n=%lld must be a multiple of 8", fn, (long long)n);
+  if ((uint64_t)first_bits + (uint64_t)n > ((uint64_t)1 << 32))
+    return fail(W4_ERR_INVALID, "%s: range of %lld patterns from 0x%08x passes 2^32", fn, (long long)n, first_bits);
+  if (n == 0) return ok();
+  if (!codes) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(W4_ERR_ALIGN, "%s: codes must be 8-byte aligned", fn);
+  return hip_status(w4::launch_fp8_encode_range(first_bits, n, codes, static_cast<hipStream_t>(stream)), fn);
 }
 
 int w4_pack_nibbles(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, void* stream) {

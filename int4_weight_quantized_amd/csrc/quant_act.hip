@@ -308,6 +308,26 @@ __global__ __launch_bounds__(kQThreads) void quant_act_asym_kernel(const uint16_
   for (int c = t + kQCache * kQThreads; c < nchunks; c += kQThreads) emit(c, buffer_load16(xrs, 16u * (uint32_t)c));
 }
 
+// Test hook of the FP8 encode: the fp32 values with bit patterns first,
+// first + 1, ..., first + n - 1 (n a multiple of 8) go through the
+// quantizer's own clamp to +-448 and pair conversion to E4M3, 8 per thread.
+__global__ __launch_bounds__(kQThreads) void fp8_encode_range_kernel(uint32_t first, int64_t n8, uint8_t* __restrict__ codes) {
+  const int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x;   // 8-value chunk
+  if (i >= n8) return;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = clamp448(__uint_as_float(first + (uint32_t)(8 * i + e)));
+  *reinterpret_cast<v2i*>(codes + 8 * i) = pack_fp8(v);
+}
+
+hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* codes, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(fp8_encode_range_kernel, dim3((unsigned)((n8 + kQThreads - 1) / kQThreads)), dim3(kQThreads), 0,
+                     stream, first, n8, codes);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, void* codes,
                                  float* scales, float* offsets, hipStream_t stream) {
   if (M == 0) return hipSuccess;

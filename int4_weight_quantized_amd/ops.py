@@ -46,6 +46,7 @@ _SIGS = {
     "w4a8_quantize_act_asym": [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P],
     "w4a8_weight_offsets": [_P, _P, _I, _I64, _I64, _I64, _P, _P],
     "w4a8_gemm_asym": [_P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _I, _I64, _I64, _I64, _P],
+    "w4_fp8_encode_range": [ctypes.c_uint32, _I64, _P, _P],
     "w4_pack_nibbles": [_P, _I64, _I64, _P, _P],
     "w4_unpack_nibbles": [_P, _I64, _I64, _P, _P],
     "w4_last_error": [],
@@ -195,6 +196,15 @@ def w4_repack(src: torch.Tensor, layout: int, K: int, N: int, batch: int = 1, st
     dst = torch.empty((batch, nbytes), dtype=torch.uint8, device=src.device)
     _check("w4_repack", lib().w4_repack(_ptr(src), layout, K, N, batch, _ptr(dst), _stream(stream)))
     return dst
+
+
+def w4_fp8_encode_range(first_bits: int, n: int, out=None, device="cuda", stream=None) -> torch.Tensor:
+    """E4M3 codes (uint8 [n]) of the fp32 values with bit patterns
+    first_bits .. first_bits + n - 1, by the quantizer's own conversion."""
+    if out is None:
+        out = torch.empty((n,), dtype=torch.uint8, device=device)
+    _check("w4_fp8_encode_range", lib().w4_fp8_encode_range(first_bits, n, _ptr(out), _stream(stream)))
+    return out
 
 
 def w4_pack_nibbles(codes: torch.Tensor, out=None, stream=None) -> torch.Tensor:

@@ -109,6 +109,13 @@ int main() {
          W4_ERR_ALIGN, "pf ws align");
   expect(w4a16_prefill(p, (const uint8_t*)p, p, p, W4_F16, 64, p, 16, 256, 4096, p, (size_t)1 << 22, nullptr),
          W4_ERR_DTYPE, "pf dt");
+  // FP8 encode test hook
+  expect(w4_fp8_encode_range(0, -8, (uint8_t*)p, nullptr), W4_ERR_INVALID, "fe n");
+  expect(w4_fp8_encode_range(0, 12, (uint8_t*)p, nullptr), W4_ERR_ALIGN, "fe n8");
+  expect(w4_fp8_encode_range(0xFFFFFFF8u, 16, (uint8_t*)p, nullptr), W4_ERR_INVALID, "fe range");
+  expect(w4_fp8_encode_range(0, 8, nullptr, nullptr), W4_ERR_INVALID, "fe null");
+  expect(w4_fp8_encode_range(0, 8, (uint8_t*)p + 4, nullptr), W4_ERR_ALIGN, "fe align");
+  expect(w4_fp8_encode_range(0xFFFFFFFFu, 0, nullptr, nullptr), W4_OK, "fe empty");
   // nibble packing
   expect(w4_pack_nibbles((const uint8_t*)p, 4, 255, (uint8_t*)p, nullptr), W4_ERR_ALIGN, "pk K");
   expect(w4_pack_nibbles((const uint8_t*)p, -1, 256, (uint8_t*)p, nullptr), W4_ERR_INVALID, "pk N");

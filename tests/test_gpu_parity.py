@@ -114,6 +114,28 @@ def test_quant_fp8_every_bf16_pattern_and_group_sums():
     assert np.all(np.abs(gs.cpu().numpy() - want) <= 1e-6 * scale + 1e-30)
 
 
+@pytest.mark.parametrize("sign", [0, 1])
+def test_fp8_encode_every_finite_fp32(sign):
+    """The quantizer's fp32 -> E4M3 step (clamp to +-448, hardware conversion)
+    on every finite fp32 of one sign, 2^31 - 2^23 inputs: the GPU codes are
+    cut into runs of equal code, and the oracle's encoder must give that code
+    at both ends of every run; with its code monotone in |v| (a CPU pin) it
+    then agrees at every input."""
+    first, n = sign << 31, 0x7F800000
+    print(f"\n[fp8 encode] sign={sign} patterns=0x{first:08x}..+0x{n:08x}", flush=True)
+    codes = ops.w4_fp8_encode_range(first, n, device=DEV)
+    starts = (torch.nonzero(codes[1:] != codes[:-1]).flatten() + 1).cpu().numpy()
+    starts = np.concatenate([[0], starts]).astype(np.int64)
+    ends = np.append(starts[1:] - 1, n - 1)
+    run_codes = codes[torch.from_numpy(starts).to(DEV)].cpu().numpy()
+    del codes
+    assert len(starts) == 127                      # one run per code 0x00..0x7E of the sign
+    for a, b, c in zip(starts, ends, run_codes):
+        v = (np.array([a, b], dtype=np.uint64) + first).astype(np.uint32).view(np.float32)
+        got = O.e4m3_encode(v)
+        assert got[0] == c and got[1] == c, (hex(first + int(a)), hex(first + int(b)), hex(int(c)), got)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("K", [128, 384, 16512])
 def test_quant_fp8_edges(dtype, K):

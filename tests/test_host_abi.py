@@ -33,14 +33,15 @@ def test_header_declares_the_boundary():
                  "w4_quantize_groupwise", "w4a16_embedding", "w4a8_quantize_act_static", "w4a16_dequantize",
                  "w4a8_quantize_act_asym", "w4a8_weight_offsets", "w4a8_gemm_asym",
                  "w4_pack_nibbles", "w4_unpack_nibbles", "w4a16_prefill_gemm", "w4a16_prefill",
-                 "w4a16_prefill_workspace_bytes", "w4_linear_noalloc", "w4_last_error", "w4_version"):
+                 "w4a16_prefill_workspace_bytes", "w4_linear_noalloc", "w4_fp8_encode_range", "w4_last_error",
+                 "w4_version"):
         assert must in names
 
 
 def test_library_exports_every_declared_symbol(L):
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert L.w4_version() == 101
+    assert L.w4_version() == 102
 
 
 def _err(L):
@@ -186,6 +187,16 @@ def test_nibble_entry_points_validate(L):
         assert fn(p(256 + 8), 4, 8, p(256), None) == -2              # misaligned
         assert fn(None, 0, 8, None, None) == 0 and fn(None, 4, 0, None, None) == 0   # empty
         assert fn(p(256), 1 << 30, 1 << 12, p(256), None) == -5      # too large
+
+
+def test_fp8_encode_range_validates(L):
+    p = ctypes.c_void_p
+    assert L.w4_fp8_encode_range(0, -8, p(256), None) == -1          # negative
+    assert L.w4_fp8_encode_range(0, 12, p(256), None) == -2          # not a multiple of 8
+    assert L.w4_fp8_encode_range(0xFFFFFFF8, 16, p(256), None) == -1 and "2^32" in _err(L)
+    assert L.w4_fp8_encode_range(0, 8, None, None) == -1             # null
+    assert L.w4_fp8_encode_range(0, 8, p(260), None) == -2           # misaligned
+    assert L.w4_fp8_encode_range(0xFFFFFFFF, 0, None, None) == 0     # empty
 
 
 def test_noalloc_scratch_limit(L):

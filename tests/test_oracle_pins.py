@@ -157,6 +157,25 @@ def test_e4m3_encode_is_nearest_even_bruteforce():
         assert int(c) == want, (float(x), hex(int(c)), hex(want))
 
 
+def test_e4m3_encode_is_monotone_in_magnitude():
+    """The encoder's code (sign bit aside) never decreases as |v| grows, and
+    the sign bit is the input's. Over random finite patterns of both signs
+    (sorted by magnitude), every power of two and its neighbours, and both
+    zeros. The exhaustive GPU check of the encode relies on it: a run of equal
+    GPU codes whose two ends the oracle maps to that code is then matched by
+    the oracle at every point in between."""
+    rng = np.random.default_rng(11)
+    mags = rng.integers(0, 0x7F800000, 400_000, dtype=np.uint32)
+    p2 = (np.arange(1, 255, dtype=np.uint32) << 23)
+    mags = np.unique(np.concatenate([mags, p2, p2 - 1, p2 + 1, np.array([0, 1, 0x7F7FFFFF], np.uint32)]))
+    for sign in (0, 1):
+        v = (mags | np.uint32(sign << 31)).view(np.float32)
+        c = O.e4m3_encode(v)
+        assert np.all((c >> 7) == sign)
+        assert np.all(np.diff((c & 0x7F).astype(np.int32)) >= 0)
+        assert (c[0] & 0x7F) == 0 and (c[-1] & 0x7F) == 0x7E
+
+
 def test_fp8_act_quant_rows():
     rng = np.random.default_rng(11)
     x = rng.standard_normal((32, 200)).astype(np.float32)
