@@ -17,9 +17,11 @@ Measured in the same run and reported beside it:
           top-8): FP8 quantization + grouped GEMM
   prefill W4A16 prefill (M=4096): dequantize to bf16 + the library's bf16
           GEMM, with the platform GEMM (hipBLASLt) timed on the same weights
-  platform_refs  hipBLASLt int8 / bf16 GEMMs at 8192^3 and a 1 GiB device
-          copy measured on this GPU beside the nominal peaks; references,
-          not ceilings (a hand-written kernel can beat the library's)
+  platform_refs  hipBLASLt int8 / bf16 GEMMs at 8192^3, a 1 GiB device copy
+          and pure-MFMA loops (int8, fp8, bf16: the matrix core's measured
+          peak, and the engine clock it implies) measured on this GPU beside
+          the nominal peaks; each GEMM object also carries its fraction of
+          the measured MFMA-only rate
   roofline  the dominant kernel (the W4A8 GEMM) against the int8 MFMA peak,
           its duration from HIP events on the launch stream
   cpu_baseline  the CPU oracle timed on a bounded row sample of the step
@@ -434,9 +436,27 @@ def main():
         (t_cp,), _, _ = timed([lambda: dst.copy_(src)], 10, 3)
         mp["copy_gbs"] = 2.0 * (1 << 30) / (t_cp * 1e-3) / 1e9      # bytes read + written
         del src, dst
-        measured = {"what": "hipBLASLt int8 and bf16 GEMMs at 8192^3 and a 1 GiB device copy (read + write); "
-                            "references measured on this GPU, not ceilings",
+        # the matrix core's measured peak: pure MFMA loops with no memory
+        # traffic (int8, fp8, bf16); the nominal peaks are quoted at 2.4 GHz,
+        # so the int8 loop's rate also gives the engine clock it ran at
+        sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+        for kind, key in ((0, "mfma_only_int8_tops"), (1, "mfma_only_fp8_tflops"), (2, "mfma_only_bf16_tflops")):
+            n_ops = ops.w4_probe_mfma(kind, 4096, sink)
+            (t_pk,), _, _ = timed([lambda kind=kind: ops.w4_probe_mfma(kind, 4096, sink)], 10, 3)
+            mp[key] = n_ops / (t_pk * 1e-3) / 1e12
+        mp["sclk_est_ghz"] = 2.4 * mp["mfma_only_int8_tops"] / PEAK_INT8_TOPS
+        del sink
+        measured = {"what": "hipBLASLt int8 and bf16 GEMMs at 8192^3, a 1 GiB device copy (read + write) and "
+                            "pure-MFMA loops (the matrix core's measured peak; sclk_est_ghz = 2.4 GHz x its "
+                            "int8 rate / the nominal int8 peak), measured on this GPU",
                     **mp}
+        w4a8["gemm_frac_mfma_only_int8"] = tops_gemm / mp["mfma_only_int8_tops"]
+        if down:
+            down["gemm_frac_mfma_only_int8"] = down["gemm_tops"] / mp["mfma_only_int8_tops"]
+        if moe:
+            moe["gemm_frac_mfma_only_fp8"] = moe["gemm_tflops"] / mp["mfma_only_fp8_tflops"]
+        if prefill:
+            prefill["gemm_frac_mfma_only_bf16"] = prefill["gemm_tflops"] / mp["mfma_only_bf16_tflops"]
         if "int8_gemm_tops" in mp:
             w4a8["gemm_vs_hipblaslt_int8"] = tops_gemm / mp["int8_gemm_tops"]
             if down:

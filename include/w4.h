@@ -469,6 +469,22 @@ int w4_quantize_groupwise(const void* w, int w_dtype, int64_t N, int64_t K, int6
 int w4a16_embedding(const int32_t* ids, int64_t T, const void* w_tiled, const void* sz_tiled,
                     int64_t group, int64_t V, int64_t K, void* out, void* stream);
 
+/*
+ * Measurement support: the matrix core's measured peak on this GPU. Pure
+ * MFMA loops with no memory traffic (1024 blocks of 256 threads, eight
+ * independent accumulator chains per wave, iters iterations), kind 0:
+ * v_mfma_i32_16x16x64_i8, 1: v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3), 2:
+ * v_mfma_f32_16x16x32_bf16. The rates the GEMMs reach are reported against
+ * it beside the nominal peaks.
+ *   iters       1 .. 2^24
+ *   sink        device int32 [sink_elems], sink_elems >= 1024 * 256; receives
+ *               a value per thread that depends on every chain
+ *   ops         host: set to the operations one launch performs
+ *               (2 * 16 * 16 * K per MFMA, K = 64, 128 or 32)
+ * Errors: INVALID, ALIGN, HIP.
+ */
+int w4_probe_mfma(int kind, int64_t iters, int32_t* sink, int64_t sink_elems, double* ops, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* w4_last_error(void);
 

@@ -23,6 +23,9 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const float* a_scale, const void* w
 hipError_t launch_quant_act_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, void* codes,
                                  float* scales, float* offsets, hipStream_t stream);
 hipError_t launch_fp8_encode_range(uint32_t first, int64_t n, uint8_t* codes, hipStream_t stream);
+double probe_mfma_ops(int kind, int64_t iters);
+int64_t probe_sink_elems();
+hipError_t launch_probe_mfma(int kind, int64_t iters, int32_t* sink, hipStream_t stream);
 hipError_t launch_weight_offsets(const void* w_tiled, const void* w_scale, int64_t group, int64_t K, int64_t N,
                                  float* out, hipStream_t stream);
 void w4a16_tiled_bytes(int64_t K, int64_t N, size_t* wbytes, size_t* szbytes);
@@ -104,7 +107,7 @@ extern "C" {
 
 const char* w4_last_error(void) { return g_err; }
 
-int w4_version(void) { return 102; }
+int w4_version(void) { return 103; }
 
 static int quantize_act(const char* fn, const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, void* codes,
                         int code_dtype, float* scales, float* group_sums, int64_t group, const float* static_scale,
@@ -675,6 +678,20 @@ int w4_fp8_encode_range(uint32_t first_bits, int64_t n, uint8_t* codes, void* st
   if (!codes) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
   if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(W4_ERR_ALIGN, "%s: codes must be 8-byte aligned", fn);
   return hip_status(w4::launch_fp8_encode_range(first_bits, n, codes, static_cast<hipStream_t>(stream)), fn);
+}
+
+int w4_probe_mfma(int kind, int64_t iters, int32_t* sink, int64_t sink_elems, double* ops, void* stream) {
+  const char* fn = "w4_probe_mfma";
+  if (kind < 0 || kind > 2) return fail(W4_ERR_INVALID, "%s: kind %d is not 0 (int8), 1 (fp8) or 2 (bf16)", fn, kind);
+  if (iters < 1 || iters > ((int64_t)1 << 24))
+    return fail(W4_ERR_INVALID, "%s: iters=%lld outside [1, 2^24]", fn, (long long)iters);
+  if (!sink || !ops) return fail(W4_ERR_INVALID, "%s: null pointer argument", fn);
+  if (sink_elems < w4::probe_sink_elems())
+    return fail(W4_ERR_INVALID, "%s: sink of %lld int32 is smaller than the %lld needed", fn, (long long)sink_elems,
+                (long long)w4::probe_sink_elems());
+  if (reinterpret_cast<uintptr_t>(sink) & 3u) return fail(W4_ERR_ALIGN, "%s: sink must be 4-byte aligned", fn);
+  *ops = w4::probe_mfma_ops(kind, iters);
+  return hip_status(w4::launch_probe_mfma(kind, iters, sink, static_cast<hipStream_t>(stream)), fn);
 }
 
 int w4_pack_nibbles(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, void* stream) {

@@ -47,6 +47,7 @@ _SIGS = {
     "w4a8_weight_offsets": [_P, _P, _I, _I64, _I64, _I64, _P, _P],
     "w4a8_gemm_asym": [_P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _I, _I64, _I64, _I64, _P],
     "w4_fp8_encode_range": [ctypes.c_uint32, _I64, _P, _P],
+    "w4_probe_mfma": [_I, _I64, _P, _I64, ctypes.POINTER(ctypes.c_double), _P],
     "w4_pack_nibbles": [_P, _I64, _I64, _P, _P],
     "w4_unpack_nibbles": [_P, _I64, _I64, _P, _P],
     "w4_last_error": [],
@@ -205,6 +206,14 @@ def w4_fp8_encode_range(first_bits: int, n: int, out=None, device="cuda", stream
         out = torch.empty((n,), dtype=torch.uint8, device=device)
     _check("w4_fp8_encode_range", lib().w4_fp8_encode_range(first_bits, n, _ptr(out), _stream(stream)))
     return out
+
+
+def w4_probe_mfma(kind: int, iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Launch the pure-MFMA loop (0 int8, 1 fp8, 2 bf16); returns its op count."""
+    ops_ = ctypes.c_double(0.0)
+    _check("w4_probe_mfma", lib().w4_probe_mfma(kind, iters, _ptr(sink), sink.numel(), ctypes.byref(ops_),
+                                                _stream(stream)))
+    return ops_.value
 
 
 def w4_pack_nibbles(codes: torch.Tensor, out=None, stream=None) -> torch.Tensor:

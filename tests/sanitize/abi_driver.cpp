@@ -116,6 +116,13 @@ int main() {
   expect(w4_fp8_encode_range(0, 8, nullptr, nullptr), W4_ERR_INVALID, "fe null");
   expect(w4_fp8_encode_range(0, 8, (uint8_t*)p + 4, nullptr), W4_ERR_ALIGN, "fe align");
   expect(w4_fp8_encode_range(0xFFFFFFFFu, 0, nullptr, nullptr), W4_OK, "fe empty");
+  // MFMA peak probe
+  double ops = 0.0;
+  expect(w4_probe_mfma(3, 16, (int32_t*)p, 1 << 20, &ops, nullptr), W4_ERR_INVALID, "pm kind");
+  expect(w4_probe_mfma(0, 0, (int32_t*)p, 1 << 20, &ops, nullptr), W4_ERR_INVALID, "pm iters");
+  expect(w4_probe_mfma(0, 16, (int32_t*)p, 16, &ops, nullptr), W4_ERR_INVALID, "pm sink");
+  expect(w4_probe_mfma(0, 16, (int32_t*)odd, 1 << 20, &ops, nullptr), W4_ERR_ALIGN, "pm align");
+  expect(w4_probe_mfma(0, 16, (int32_t*)p, 1 << 20, nullptr, nullptr), W4_ERR_INVALID, "pm ops");
   // nibble packing
   expect(w4_pack_nibbles((const uint8_t*)p, 4, 255, (uint8_t*)p, nullptr), W4_ERR_ALIGN, "pk K");
   expect(w4_pack_nibbles((const uint8_t*)p, -1, 256, (uint8_t*)p, nullptr), W4_ERR_INVALID, "pk N");

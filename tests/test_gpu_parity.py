@@ -718,3 +718,16 @@ def test_w4a8_asym_up_proj_rows():
     rows = np.sort(np.random.default_rng(8).choice(d["M"], 32, replace=False))
     ref = O.w4a8_reference_asym(d["x"], d["x_dtype"], d["qweight"], d["scales"], d["group"], rows=rows)
     assert_close(to_f64(y[torch.from_numpy(rows).to(DEV)]), ref["y"], "w4a8 asym up_proj")
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_probe_mfma_runs(kind):
+    """The measured-peak loop (measurement support, not a hot-path kernel):
+    it runs, reports the op count of its documented shape and writes every
+    thread's value."""
+    sink = torch.full((1024 * 256,), -7, dtype=torch.int32, device=DEV)
+    n_ops = ops.w4_probe_mfma(kind, 3, sink)
+    torch.cuda.synchronize()
+    k = {0: 64, 1: 128, 2: 32}[kind]
+    assert n_ops == 1024 * 4 * 8 * 3 * 2 * 16 * 16 * k
+    assert int((sink == -7).sum()) < sink.numel() // 2

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
                  "w4_quantize_groupwise", "w4a16_embedding", "w4a8_quantize_act_static", "w4a16_dequantize",
                  "w4a8_quantize_act_asym", "w4a8_weight_offsets", "w4a8_gemm_asym",
                  "w4_pack_nibbles", "w4_unpack_nibbles", "w4a16_prefill_gemm", "w4a16_prefill",
-                 "w4a16_prefill_workspace_bytes", "w4_linear_noalloc", "w4_fp8_encode_range", "w4_last_error",
+                 "w4a16_prefill_workspace_bytes", "w4_linear_noalloc", "w4_fp8_encode_range", "w4_probe_mfma", "w4_last_error",
                  "w4_version"):
         assert must in names
 
@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert L.w4_version() == 102
+    assert L.w4_version() == 103
 
 
 def _err(L):
@@ -197,6 +197,17 @@ def test_fp8_encode_range_validates(L):
     assert L.w4_fp8_encode_range(0, 8, None, None) == -1             # null
     assert L.w4_fp8_encode_range(0, 8, p(260), None) == -2           # misaligned
     assert L.w4_fp8_encode_range(0xFFFFFFFF, 0, None, None) == 0     # empty
+
+
+def test_probe_mfma_validates(L):
+    p = ctypes.c_void_p
+    ops_ = ctypes.c_double(0.0)
+    assert L.w4_probe_mfma(3, 16, p(256), 1 << 20, ctypes.byref(ops_), None) == -1      # kind
+    assert L.w4_probe_mfma(0, 0, p(256), 1 << 20, ctypes.byref(ops_), None) == -1       # iters
+    assert L.w4_probe_mfma(0, 16, None, 1 << 20, ctypes.byref(ops_), None) == -1        # null sink
+    assert L.w4_probe_mfma(0, 16, p(256), 1 << 10, ctypes.byref(ops_), None) == -1      # small sink
+    assert L.w4_probe_mfma(0, 16, p(258), 1 << 20, ctypes.byref(ops_), None) == -2      # misaligned
+    assert ops_.value == 0.0                    # nothing set on a refused call
 
 
 def test_noalloc_scratch_limit(L):
