@@ -221,7 +221,8 @@ __global__ __launch_bounds__(kDThreads * WPW, 1) void w4a16_kernel(
 
 // Few rows (M <= 4) over K <= 4096 (at most 8 windows): one row tile per
 // block, one window per wave (NWV = 4 waves for K <= 2048, else 8). Every
-// block is resident at once (<= 64 VGPRs), and each wave issues all of its
+// block of a 14336-row matrix is resident at once (46-66 VGPRs: seven or
+// eight waves per SIMD, 896 blocks of eight waves), and each wave issues all of its
 // loads up front -- its activation rows, then its scale/zero pairs, then
 // its 4 KiB of weights -- so the matrix is requested in a single pass with
 // no chain of tiles behind any block, and the work left once a wave's
