@@ -327,7 +327,9 @@ def test_w4a16_decode_workload(M):
     # partial last window, a wave with no second window, four rows
     (1, 3200, 200, 64, True), (2, 4096, 136, 128, False), (4, 2560, 264, 256, True), (3, 3584, 40, 64, True),
     # two row tiles per block (5 to 8 rows), an odd tile count
-    (6, 2048, 264, 128, True), (7, 4096, 40, 256, False), (5, 1536, 1032, 64, True)])
+    (6, 2048, 264, 128, True), (7, 4096, 40, 256, False), (5, 1536, 1032, 64, True),
+    # the one-row-tile kernel's four-wave form over many row tiles (tied-head shapes), a partial last tile
+    (3, 2048, 16392, 64, True), (2, 1024, 32776, 128, False), (4, 2048, 8200, 512, True)])
 def test_w4a16_edges(M, K, N, group, zero):
     d = W.w4a16_inputs(M, K, N, group, seed=M + K + N)
     y = _w4a16_run(d, with_zero=zero)
